@@ -1,0 +1,354 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these compares the oracle with itself: every expected value comes
+from a golden fixture quoting the pages, a closed form, an invariant, a
+library routine (numpy / torch), or the independent brute force in
+``tests/_bruteforce.py``.
+"""
+from __future__ import annotations
+
+import math
+import os
+import struct
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import qmoe_synth as synth
+from tests import _bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    fields = {}
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            head, *rest = line.split()
+            try:
+                rows.append([float(head)] + [float(v) for v in rest])
+            except ValueError:
+                fields[head] = rest
+    return fields, rows
+
+
+def _pack_bitstream(values, bits):
+    """Pack small unsigned ints into a little-endian bit stream (test-side encoder)."""
+    stream = np.zeros(len(values) * bits, dtype=np.uint8)
+    for i, v in enumerate(values):
+        for b in range(bits):
+            stream[i * bits + b] = (int(v) >> b) & 1
+    pad = (-len(stream)) % 8
+    stream = np.concatenate([stream, np.zeros(pad, dtype=np.uint8)])
+    return np.packbits(stream, bitorder="little")
+
+
+# ---------------------------------------------------------------- widening
+def test_fp16_widening_matches_numpy_for_every_pattern():
+    pats = np.arange(1 << 16, dtype=np.uint16)
+    got = oracle.widen(pats, 1)
+    ref = pats.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_bf16_widening_matches_torch_for_every_pattern():
+    pats = np.arange(1 << 16, dtype=np.uint16)
+    got = oracle.widen(pats, 2)
+    ref = torch.from_numpy(pats.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+# ---------------------------------------------------------------- unpacking
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_unpack_matches_little_endian_bitstream(bits):
+    rng = np.random.default_rng(7 + bits)
+    K = 256
+    codes = rng.integers(0, 256, size=(5, K * bits // 8), dtype=np.uint8)
+    q, _ = oracle.dequant(codes, np.zeros((5, K // 32), np.uint16), None, K, bits, 32,
+                          math.nan, 1, want_weights=False)
+    assert np.array_equal(q, bf.unpack_bitstream(codes, bits, K))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_pack_unpack_round_trip(bits):
+    rng = np.random.default_rng(11 + bits)
+    K = 128
+    vals = rng.integers(0, 1 << bits, size=K)
+    packed = _pack_bitstream(vals, bits)[None, :]
+    q, _ = oracle.dequant(packed, np.zeros((1, K // 16), np.uint16), None, K, bits, 16,
+                          math.nan, 1, want_weights=False)
+    assert np.array_equal(q[0], vals)
+
+
+def test_int3_group_layout_is_24_bit_little_endian_word():
+    # one 3-byte group holding codes 0..7 in order: word = sum j << 3j
+    word = sum(j << (3 * j) for j in range(8))
+    group = np.array([[word & 0xFF, (word >> 8) & 0xFF, (word >> 16) & 0xFF]], dtype=np.uint8)
+    q, _ = oracle.dequant(group, np.zeros((1, 1), np.uint16), None, 8, 3, 8, math.nan, 1,
+                          want_weights=False)
+    assert list(q[0]) == list(range(8))
+
+
+# ---------------------------------------------------------------- zero points
+def test_fractional_zero_point_worked_example():
+    fields, _ = _golden("fractional_zero_point_int2.txt")
+    bits = int(fields["bits"][0])
+    zpo = float(fields["zero_point_offset"][0])
+    codes = [int(v) for v in fields["codes"]]
+    expect = [float(v) for v in fields["dequant_over_scale"]]
+    # 16 elements: the four codes repeated, one block of 16, scale 0.01 in fp16
+    vals = codes * 4
+    packed = _pack_bitstream(vals, bits)[None, :]
+    scale = np.array([[np.float16(0.01)]], dtype=np.float16).view(np.uint16)
+    q, w = oracle.dequant(packed, scale, None, 16, bits, 16, zpo, 1)
+    s = float(np.float16(0.01))
+    assert list(q[0, :4]) == codes
+    assert np.array_equal(w[0, :4], np.array(expect) * s)
+
+
+def test_symmetric_centres():
+    _, rows = _golden("symmetric_centres.txt")
+    for bits_f, centre in rows:
+        bits = int(bits_f)
+        vals = [int(centre)] * 8 + [0] * 8
+        packed = _pack_bitstream(vals, bits)[None, :]
+        scale = np.array([[np.float16(0.5)]], dtype=np.float16).view(np.uint16)
+        _, w = oracle.dequant(packed, scale, None, 16, bits, 16, math.nan, 1)
+        assert np.all(w[0, :8] == 0.0)
+        assert np.all(w[0, 8:] == -centre * 0.5)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_uint8_zero_points_take_precedence_over_offset(bits):
+    rng = np.random.default_rng(3)
+    K, bs = 64, 16
+    nb = K // bs
+    codes = rng.integers(0, 256, size=(3, K * bits // 8), dtype=np.uint8)
+    zvals = rng.integers(0, 1 << bits, size=(3, nb))
+    if bits == 3:
+        zp = zvals.astype(np.uint8)
+    else:
+        zp = np.stack([_pack_bitstream(r, bits) for r in zvals])
+    scales = np.full((3, nb), np.float16(1.0), dtype=np.float16).view(np.uint16)
+    q, w = oracle.dequant(codes, scales, zp, K, bits, bs, 1.5, 1)
+    expect = q - np.repeat(zvals, bs, axis=1)
+    assert np.array_equal(w, expect.astype(np.float64))
+
+
+def test_dequant_matches_dense_bruteforce_all_modes():
+    rng = np.random.default_rng(5)
+    for bits in (2, 3, 4):
+        for dtype in (1, 2):
+            for mode in ("sym", "zpo", "u8"):
+                K, bs, N = 128, 32, 6
+                codes = rng.integers(0, 256, size=(2, N, K * bits // 8), dtype=np.uint8)
+                s32 = rng.uniform(0.005, 0.02, size=(2, N, K // bs)).astype(np.float32)
+                scales = synth._to_dtype_bits(s32, dtype)
+                zp = None
+                zpo = math.nan
+                if mode == "u8":
+                    zp = synth._draw_zero_points(rng, 2, N, K // bs, bits, 0, (1 << bits) - 1)
+                elif mode == "zpo":
+                    zpo = 1.5 if bits == 2 else 3.25
+                _, w = oracle.dequant(codes, scales, zp, K, bits, bs, zpo, dtype)
+                ref = bf.dense_weights(codes, scales, zp, K, bits, bs, zpo, dtype)
+                assert np.array_equal(w, ref), (bits, dtype, mode)
+
+
+# ---------------------------------------------------------------- routing
+def _adversarial_logits():
+    nan_pos = struct.unpack("<f", struct.pack("<I", 0x7FC00001))[0]
+    nan_pos_big = struct.unpack("<f", struct.pack("<I", 0x7FFFFFFF))[0]
+    nan_neg = struct.unpack("<f", struct.pack("<I", 0xFFC00000))[0]
+    nan_neg_big = struct.unpack("<f", struct.pack("<I", 0xFFFFFFFF))[0]
+    inf = float("inf")
+    rows = [
+        [0.0, -0.0, 0.0, -0.0, 1.0, -1.0, 0.0, -0.0],
+        [-0.0, -0.0, 0.0, -1e-45, 1e-45, -inf, inf, 0.0],
+        [nan_pos, inf, nan_neg, -inf, 3.0, nan_pos_big, nan_neg_big, 2.0],
+        [1.5] * 8,
+        [-inf] * 8,
+        [nan_neg, nan_neg_big, -inf, -3.4e38, -1.0, -1e-38, -0.0, nan_neg],
+        [2.0, 2.0, 1.0, 2.0, 1.0, 3.0, 3.0, 1.0],
+        [nan_pos, nan_pos, nan_pos_big, nan_pos_big, 0.0, 0.0, -0.0, -0.0],
+    ]
+    return np.array(rows, dtype=np.float32)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5, 8])
+def test_route_ids_match_ieee_total_order_bruteforce(k):
+    rng = np.random.default_rng(k)
+    logits = np.concatenate([_adversarial_logits(),
+                             rng.standard_normal((40, 8)).astype(np.float32),
+                             np.round(rng.standard_normal((40, 8)) * 2).astype(np.float32)])
+    ids, _ = oracle.route(logits, k, 1)
+    assert np.array_equal(ids, bf.route(logits, k))
+
+
+def test_route_key_orders_like_total_order():
+    rng = np.random.default_rng(9)
+    vals = list(_adversarial_logits().reshape(-1)) + list(
+        rng.standard_normal(200).astype(np.float32))
+    for a in vals[:60]:
+        for b in vals[::7]:
+            ka, kb = oracle.route_key(a), oracle.route_key(b)
+            pa, pb = bf.total_order_position(float(a)), bf.total_order_position(float(b))
+            assert (ka < kb) == (pa < pb) and (ka == kb) == (pa == pb)
+
+
+def test_route_all_equal_logits_picks_lowest_indices():
+    logits = np.full((4, 16), 0.25, dtype=np.float32)
+    for k in (1, 4, 16):
+        ids, w = oracle.route(logits, k, 1)
+        assert np.array_equal(ids, np.tile(np.arange(k), (4, 1)))
+        assert np.allclose(w, 1.0 / k, rtol=0, atol=1e-15)
+
+
+def test_route_k_equals_e_is_a_permutation_and_softmax():
+    rng = np.random.default_rng(21)
+    logits = rng.standard_normal((30, 12)).astype(np.float32)
+    ids, w = oracle.route(logits, 12, 0)
+    assert all(sorted(r) == list(range(12)) for r in ids.tolist())
+    ref = torch.softmax(torch.from_numpy(logits.astype(np.float64)), dim=1).numpy()
+    assert np.allclose(w, np.take_along_axis(ref, ids.astype(np.int64), 1), rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (512, 10), (64, 7), (1000, 1)])
+def test_route_weights_invariants(E, k):
+    rng = np.random.default_rng(E + k)
+    logits = (rng.standard_normal((25, E)) * 2).astype(np.float32)
+    ids, w = oracle.route(logits, k, 1)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=4e-16 * k)
+    # the best expert's numerator is exp(0) = 1, so w0 = 1 / sum
+    assert np.all(np.diff(w, axis=1) <= 0)
+    ref = bf.route_weights(logits, ids, 1)
+    assert np.allclose(w, ref, rtol=1e-14, atol=0)
+    ids_u, w_u = oracle.route(logits, k, 0)
+    assert np.array_equal(ids_u, ids)
+    assert np.allclose(w_u, bf.route_weights(logits, ids, 0), rtol=1e-13, atol=0)
+    assert np.all(w_u.sum(axis=1) <= 1.0 + 1e-15)
+
+
+def test_route_top1_normalized_weight_is_exactly_one():
+    rng = np.random.default_rng(4)
+    logits = rng.standard_normal((50, 32)).astype(np.float32)
+    _, w = oracle.route(logits, 1, 1)
+    assert np.all(w == 1.0)
+
+
+# ---------------------------------------------------------------- grouping
+@pytest.mark.parametrize("E,R,m_tile,n_tile,N", [(8, 64, 16, 64, 200), (512, 60, 16, 32, 64),
+                                                 (3, 1, 128, 128, 128), (8, 1000, 128, 256, 4096),
+                                                 (5, 0, 16, 16, 16)])
+def test_group_matches_python_sort(E, R, m_tile, n_tile, N):
+    rng = np.random.default_rng(R + E)
+    ids = rng.integers(0, E, size=R).astype(np.int32)
+    if R > 3:
+        ids[::5] = 0  # crowd one expert
+    off, srt, wl, n = oracle.group(ids, E, m_tile, n_tile, N)
+    boff, bsrt, bwl = bf.group(ids, E, m_tile, n_tile, N)
+    assert np.array_equal(off, boff) and np.array_equal(srt, bsrt)
+    assert n == len(bwl) and np.array_equal(wl, bwl)
+    assert off[E] == R
+
+
+def test_group_skips_out_of_range_ids():
+    ids = np.array([3, -1, 0, 7, 3, 2, 9], dtype=np.int32)
+    off, srt, wl, n = oracle.group(ids, 4, 2, 8, 8)
+    boff, bsrt, bwl = bf.group(ids, 4, 2, 8, 8)
+    assert np.array_equal(off, boff) and np.array_equal(srt, bsrt) and np.array_equal(wl, bwl)
+    assert off[4] == 4
+
+
+# ---------------------------------------------------------------- the layer
+LAYER_CASES = [
+    dict(T=5, H=64, I=32, E=4, k=2, fc1_bits=4, fc2_bits=4, block_size=16, dtype=1, act=0),
+    dict(T=4, H=32, I=64, E=3, k=3, fc1_bits=2, fc2_bits=2, block_size=32, dtype=1, act=1,
+         zp_mode="zpo", zpo=1.5),
+    dict(T=6, H=64, I=48, E=6, k=2, fc1_bits=3, fc2_bits=2, block_size=16, dtype=2, act=0),
+    dict(T=3, H=48, I=32, E=5, k=4, fc1_bits=4, fc2_bits=3, block_size=16, dtype=2, act=1,
+         zp_mode="u8", zp_range=(0, 7)),
+    dict(T=7, H=32, I=32, E=8, k=1, fc1_bits=2, fc2_bits=4, block_size=32, dtype=1, act=0,
+         normalize=0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LAYER_CASES)))
+def test_layer_matches_dense_bruteforce(case):
+    spec = synth.custom(**LAYER_CASES[case])
+    inp = synth.make_inputs(spec, 100 + case)
+    got = oracle.forward(inp, spec)
+    ref = bf.layer(inp, spec)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_layer_token_subset_equals_full_rows():
+    spec = synth.custom(**LAYER_CASES[2])
+    inp = synth.make_inputs(spec, 55)
+    full = oracle.forward(inp, spec)
+    sub = oracle.forward(inp, spec, tokens=np.array([5, 0, 3]))
+    assert np.array_equal(sub, full[[5, 0, 3]])
+
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_single_expert_top1_is_dense_gated_ffn(act):
+    # E=1, k=1, normalize=1: weight is exactly 1 and the layer is the textbook
+    # W2 (act(Wg x) * (Wu x)) with Wg the even and Wu the odd fc1 rows.
+    spec = synth.custom(T=6, H=64, I=32, E=1, k=1, fc1_bits=4, fc2_bits=4, block_size=16,
+                        dtype=1, act=act)
+    inp = synth.make_inputs(spec, 77)
+    got = oracle.forward(inp, spec)
+    x = torch.from_numpy(bf.widen(inp["hidden"], 1))
+    w1 = torch.from_numpy(bf.dense_weights(inp["fc1_codes"], inp["fc1_scales"], None, 64, 4, 16,
+                                           math.nan, 1)[0])
+    w2 = torch.from_numpy(bf.dense_weights(inp["fc2_codes"], inp["fc2_scales"], None, 32, 4, 16,
+                                           math.nan, 1)[0])
+    wg, wu = w1[0::2], w1[1::2]
+    gate = F.gelu(x @ wg.T, approximate="tanh") if act else F.silu(x @ wg.T)
+    ref = ((gate * (x @ wu.T)) @ w2.T).numpy()
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_all_tokens_on_same_experts_is_weighted_dense_gemm():
+    spec = synth.custom(T=8, H=32, I=32, E=4, k=2, fc1_bits=4, fc2_bits=4, block_size=16, dtype=1)
+    inp = synth.make_inputs(spec, 8)
+    logits = np.tile(np.array([[0.1, 3.0, -2.0, 2.5]], np.float32), (8, 1))
+    logits[:, 1] += np.linspace(0, 0.1, 8).astype(np.float32)
+    inp["logits"] = logits
+    got = oracle.forward(inp, spec)
+    x = bf.widen(inp["hidden"], 1)
+    w1 = bf.dense_weights(inp["fc1_codes"], inp["fc1_scales"], None, 32, 4, 16, math.nan, 1)
+    w2 = bf.dense_weights(inp["fc2_codes"], inp["fc2_scales"], None, 32, 4, 16, math.nan, 1)
+    out = np.zeros((8, 32))
+    l = logits.astype(np.float64)
+    for t in range(8):
+        a, b = np.exp(l[t, 1]), np.exp(l[t, 3])
+        for e, wt in ((1, a / (a + b)), (3, b / (a + b))):
+            y1 = w1[e] @ x[t]
+            g = y1[0::2]
+            act = g / (1 + np.exp(-g)) * y1[1::2]
+            out[t] += wt * (w2[e] @ act)
+    assert np.allclose(got, out, rtol=1e-12, atol=1e-13)
+
+
+def test_named_workload_shapes():
+    # the five named workloads draw consistent shapes
+    for i in (1, 2):
+        spec = synth.workload(i)
+        inp = synth.make_inputs(spec, synth.seed_for(i))
+        E, I, H = spec["E"], spec["I"], spec["H"]
+        assert inp["fc1_codes"].shape == (E, 2 * I, H * spec["fc1_bits"] // 8)
+        assert inp["fc2_codes"].shape == (E, H, I * spec["fc2_bits"] // 8)
+        assert inp["fc1_scales"].shape == (E, 2 * I, H // spec["block_size"])
