@@ -1,0 +1,207 @@
+/*
+ * qmoe.h -- C ABI of libqmoe.so, the MI355X (gfx950) quantized
+ * Mixture-of-Experts (QMoE) FFN layer.
+ *
+ * The layer: top-k routing from router logits, expert grouping into sorted
+ * offsets and a tile work-list, a grouped fc1 projection over block-wise
+ * int2/int3/int4 packed weights dequantized in registers, a SwiGLU or GeGLU
+ * gated activation, a grouped fc2 projection, and a routing-weighted combine.
+ *
+ * Sources (page title, then the named function or paragraph):
+ *   [qmoe.rs]   docs.rs source page of onnx-runtime-ep-cuda, src/kernels/qmoe.rs
+ *   [PR 32198]  onnxruntime pull request 32198, "[CUDA] QMoE: fused int2
+ *               mixed-input GEMM + GeGLU activation + fractional zero-point"
+ *   [PR 33569]  onnxruntime pull request 33569, "[CUDA] Add fast INT3 QMoE
+ *               kernels and offline SM80 INT2/INT4 prepack support"
+ *   [gemm_quant_moe.rs]  metrale_model_layers layers/ops/gemm_quant_moe.rs
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument except `stream` is a DEVICE pointer, owned by the
+ *     caller; the library allocates nothing and frees nothing.  Tensors are
+ *     dense row-major with no padding.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the legacy default
+ *     stream.  Every call only enqueues work on `stream` and returns; nothing
+ *     synchronizes the host.  Results are valid once the stream reaches them.
+ *   - Return value: QMOE_OK (0) or a negative QMOE_ERR_* code.  All argument
+ *     checks run before any launch, so on an error nothing was enqueued and no
+ *     output was written.  qmoe_last_error() then returns a message (thread
+ *     local, valid until the next call on the same thread).
+ *   - Calls that overlap in time and share output or workspace buffers race;
+ *     the library holds no state between calls except the optional kernel
+ *     timer below.
+ *   - Route r = t*top_k + s is slot s of token t.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define QMOE_OK 0
+#define QMOE_ERR_INVALID_ARG (-1) /* bad shape, null pointer, alignment, value     */
+#define QMOE_ERR_UNSUPPORTED (-2) /* valid op, but no kernel for this combination */
+#define QMOE_ERR_WORKSPACE (-3)   /* workspace or work-list capacity too small     */
+#define QMOE_ERR_HIP (-4)         /* a HIP runtime call or launch failed           */
+
+/* activation dtypes (hidden states, scales, output) */
+#define QMOE_DTYPE_F16 1
+#define QMOE_DTYPE_BF16 2
+
+/* gated activations on interleaved fc1 rows (row 2j = gate, 2j+1 = up)
+ * [qmoe.rs, qmoe_activate with swiglu_fusion = 1; PR 32198, GeGLU "gated like
+ * SwiGLU (interleaved fc1)"] */
+#define QMOE_ACT_SWIGLU 0 /* silu(g) * u                                            */
+#define QMOE_ACT_GEGLU 1  /* 0.5 g (1 + tanh(0.7978845608028654 (g + 0.044715 g^3))) * u */
+
+/* Expanded-row count R = T*top_k at or below which qmoe_forward takes the
+ * decode path (each selected expert's weights streamed once for all of its
+ * rows); above it, the prefill grouped GEMM.  [PR 33569: GEMV dispatch for
+ * up to 80 expanded rows] */
+#define QMOE_DECODE_MAX_ROUTES 80
+
+/*
+ * One quantized projection of all E experts: N output rows of K inputs.
+ *   codes        uint8 [E, N, K*bits/8].  2- and 4-bit codes fill each byte
+ *                from the least significant bits up (code kk of a row sits in
+ *                byte kk/(8/bits) at bit (kk%(8/bits))*bits) [qmoe.rs,
+ *                decode_affine_weight].  3-bit codes come in 3-byte groups of
+ *                8: code kk is bits [3(kk%8), 3(kk%8)+3) of the little-endian
+ *                24-bit word of group kk/8 [PR 33569, 24-bit 8-code INT3
+ *                unpacking].  16-byte aligned.
+ *   scales       fp16/bf16 (the layer's dtype) [E, N, K/block_size]; block
+ *                b covers inputs [b*block_size, (b+1)*block_size).  4-byte
+ *                aligned.
+ *   zero_points  NULL, or uint8 [E, N, Z]: bits-wide values packed like the
+ *                2/4-bit codes with Z = ceil((K/block_size)/(8/bits)), or one
+ *                byte per block for bits = 3 (Z = K/block_size).
+ *   bits         2, 3 or 4.
+ * Dequantized weight: W[e,n,kk] = (code - zp) * scale[e,n,kk/block_size]
+ * where zp is the zero_points entry if the tensor is given, else the layer's
+ * zero_point_offset if it is not NaN, else the symmetric centre 2^(bits-1)
+ * [qmoe.rs, decode_affine_weight; PR 32198, zero_point_offset].
+ */
+typedef struct qmoe_proj {
+    const uint8_t* codes;
+    const void* scales;
+    const uint8_t* zero_points;
+    int32_t bits;
+} qmoe_proj;
+
+/* Message describing the last error returned on this thread ("" if none). */
+const char* qmoe_last_error(void);
+
+/*
+ * Top-k routing [qmoe.rs, total_order_key, route_value_is_better, qmoe_route].
+ *   logits        float32 [T, E]
+ *   topk_ids      int32 [T, top_k] out: the top_k experts of each token in
+ *                 descending order of the route key, equal keys to the lower
+ *                 index.  The key orders float32 bit patterns totally (-0
+ *                 below +0, +NaN above +inf, -NaN below -inf).
+ *   topk_weights  float32 [T, top_k] out: exp(l - m) / D with m the largest
+ *                 non-NaN logit of the token; D sums exp(l - m) over the
+ *                 selected experts if normalize, else over all E experts.
+ * Requires T >= 0, 1 <= E <= 1024, 1 <= top_k <= E, normalize in {0, 1}.
+ */
+int qmoe_route(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t normalize,
+               int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* Work-list capacity (items) that always suffices for qmoe_group with these
+ * arguments: (ceil(R/m_tile) + min(E, R)) * ceil(N/n_tile), R = T*top_k. */
+int64_t qmoe_worklist_capacity(int64_t T, int32_t top_k, int32_t E, int32_t m_tile,
+                               int32_t n_tile, int32_t N);
+
+/*
+ * Expert grouping and tile work-list [qmoe.rs, launch_grouping (counts,
+ * offsets, grouped routes); gemm_quant_moe.rs, moe_build_tile_worklist].
+ *   topk_ids        int32 [T*top_k] expert of each route; entries outside
+ *                   [0, E) join no group.
+ *   expert_offsets  int32 [E+1] out: exclusive prefix sum of per-expert
+ *                   route counts (offsets[E] = number of grouped routes).
+ *   sorted_routes   int32 [T*top_k] out: route ids grouped by expert, experts
+ *                   ascending, route ids ascending within an expert (stable).
+ *                   Entries at and past offsets[E] are left untouched.
+ *   worklist        int32 [worklist_capacity, 3] out: one item
+ *                   {expert, m_tile_index, n_tile_index} for every m_tile rows
+ *                   of an expert with routes times every n_tile columns of N;
+ *                   experts ascending, then m, then n.
+ *   n_items         int32 [1] out: number of items.
+ * Requires 1 <= E <= 1024, m_tile >= 1, n_tile >= 1, N >= 1, T*top_k < 2^31,
+ * worklist_capacity >= qmoe_worklist_capacity(...).  One workgroup does all
+ * of it; no atomics, so the output is deterministic.
+ */
+int qmoe_group(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int32_t m_tile,
+               int32_t n_tile, int32_t N, int32_t* expert_offsets, int32_t* sorted_routes,
+               int32_t* worklist, int64_t worklist_capacity, int32_t* n_items, void* stream);
+
+/* Workspace bytes qmoe_forward needs for these sizes (0 on invalid sizes). */
+size_t qmoe_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t top_k,
+                           int32_t dtype);
+
+/*
+ * The whole layer [qmoe.rs, QMoEKernel::execute; PR 32198; PR 33569].
+ *   hidden      dtype [T, H]           input states, 16-byte aligned
+ *   logits      float32 [T, E]         router logits
+ *   fc1         N = 2*I rows (row 2j gate, 2j+1 up), K = H
+ *   fc2         N = H rows, K = I
+ *   zero_point_offset   fractional zero point, NaN = none; finite otherwise.
+ *               Used for a projection whose zero_points is NULL.
+ *   block_size  power of two >= 16 dividing H and I
+ *   top_k, normalize    as in qmoe_route
+ *   activation  QMOE_ACT_SWIGLU or QMOE_ACT_GEGLU
+ *   dtype       QMOE_DTYPE_F16 or QMOE_DTYPE_BF16
+ *   out         dtype [T, H] out: sum over slots s (in slot order) of
+ *               w[t,s] * fc2_e(act(fc1_e(x_t))), rounded once to dtype
+ *   topk_ids_out, topk_w_out  NULL, or int32/float32 [T, top_k] copies of the
+ *               routing decision
+ *   workspace   >= qmoe_workspace_size(T, H, I, E, top_k, dtype) bytes,
+ *               256-byte aligned; contents on entry do not matter.
+ * Requires 1 <= E <= 1024, 1 <= top_k <= E, H and I multiples of 128,
+ * bits in {2,3,4} per projection.  T = 0 returns QMOE_OK and enqueues nothing.
+ * Numerics: dequantized weights are rounded to dtype (round to nearest even)
+ * before the products, products accumulate in float32, the activation is
+ * rounded to dtype, fc2 outputs stay float32 until the combine.
+ */
+int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, int32_t I,
+                 int32_t E, const qmoe_proj* fc1, const qmoe_proj* fc2, float zero_point_offset,
+                 int32_t block_size, int32_t top_k, int32_t normalize, int32_t activation,
+                 int32_t dtype, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Test hook: the dequantization the projections use, written out in full.
+ *   p           one projection as above (E experts, N rows, K inputs)
+ *   codes_out   NULL or int32 [E, N, K] out: unpacked codes
+ *   w_out       dtype [E, N, K] out: round-to-nearest-even of (code - zp) * scale
+ * The kernels that run the projections call the same device unpack and
+ * dequant routines.
+ */
+int qmoe_dequantize(const qmoe_proj* p, int32_t E, int32_t N, int32_t K, int32_t block_size,
+                    float zero_point_offset, int32_t dtype, int32_t* codes_out, void* w_out,
+                    void* stream);
+
+/*
+ * Kernel timer for measurement.  After qmoe_timer_start(stage), every
+ * qmoe_forward call records a HIP event pair on its stream around each
+ * launch of that stage's kernel (at most 4096 pairs).  qmoe_timer_stop()
+ * waits for the recorded events, stores the summed elapsed milliseconds and
+ * the number of launches timed, and disables the timer.
+ * Stages: 0 route, 1 group, 2 fc1 (+ activation), 3 fc2, 4 combine.
+ */
+#define QMOE_STAGE_ROUTE 0
+#define QMOE_STAGE_GROUP 1
+#define QMOE_STAGE_FC1 2
+#define QMOE_STAGE_FC2 3
+#define QMOE_STAGE_COMBINE 4
+int qmoe_timer_start(int32_t stage);
+int qmoe_timer_stop(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_H */

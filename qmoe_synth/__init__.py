@@ -109,6 +109,19 @@ def _draw_zero_points(rng, E, N, n_blocks, bits, lo, hi) -> np.ndarray:
     return out.astype(np.uint8)
 
 
+def _draw_logits(rng, spec) -> np.ndarray:
+    T, E = spec["T"], spec["E"]
+    logits = rng.standard_normal((T, E), dtype=np.float32) * np.float32(spec["logit_sigma"])
+    if spec.get("logit_bias") == "linspace0to2":
+        logits = logits + np.linspace(0.0, 2.0, E, dtype=np.float32)[None, :]
+    return np.ascontiguousarray(logits, dtype=np.float32)
+
+
+def make_logits(spec: dict, seed: int) -> np.ndarray:
+    """Only the router logits of ``make_inputs(spec, seed)`` (they are drawn first)."""
+    return _draw_logits(np.random.default_rng(seed), spec)
+
+
 def make_inputs(spec: dict, seed: int) -> dict:
     """Draw one layer's inputs for ``spec`` with ``numpy.random.default_rng(seed)``.
 
@@ -119,10 +132,7 @@ def make_inputs(spec: dict, seed: int) -> dict:
     T, H, I, E, bs = spec["T"], spec["H"], spec["I"], spec["E"], spec["block_size"]
     dtype = spec["dtype"]
 
-    logits = (rng.standard_normal((T, E), dtype=np.float32) * np.float32(spec["logit_sigma"]))
-    if spec.get("logit_bias") == "linspace0to2":
-        logits = logits + np.linspace(0.0, 2.0, E, dtype=np.float32)[None, :]
-    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    logits = _draw_logits(rng, spec)
 
     hidden = _to_dtype_bits(rng.standard_normal((T, H), dtype=np.float32), dtype)
 

@@ -1,0 +1,56 @@
+// combine.hip -- routing-weighted sum of the fc2 rows of each token.
+//
+// [qmoe.rs, qmoe_combine]: out[t, h] = sum over slots s = 0..k-1, in slot
+// order, of w[t, s] * y2[t*k + s, h], accumulated in float32 and rounded once
+// to the output dtype.  Each thread owns four consecutive h of one token, so
+// there are no atomics and the result is deterministic.
+#include "qmoe_device.h"
+#include "qmoe_internal.h"
+
+namespace qmoe {
+namespace {
+
+template <int DT>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y2,
+                                                      const float* __restrict__ w, int64_t T,
+                                                      int H, int top_k,
+                                                      uint16_t* __restrict__ out)
+{
+    const int64_t quads = (int64_t)H / 4;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= T * quads) return;
+    const int64_t t = idx / quads;
+    const int64_t h = (idx % quads) * 4;
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < top_k; ++s) {
+        const int64_t r = t * top_k + s;
+        const float wt = w[r];
+        const float4 v = *reinterpret_cast<const float4*>(y2 + r * H + h);
+        sum.x += wt * v.x;
+        sum.y += wt * v.y;
+        sum.z += wt * v.z;
+        sum.w += wt * v.w;
+    }
+    uint2 packed;
+    packed.x = pack2(Dt<DT>::from_float(sum.x), Dt<DT>::from_float(sum.y));
+    packed.y = pack2(Dt<DT>::from_float(sum.z), Dt<DT>::from_float(sum.w));
+    *reinterpret_cast<uint2*>(out + t * H + h) = packed;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* y2, const float* weights, int64_t T, int H, int top_k,
+                          void* out, int dtype, hipStream_t s)
+{
+    const int64_t n = T * (H / 4);
+    const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+    uint16_t* o = reinterpret_cast<uint16_t*>(out);
+    if (dtype == kBF16) {
+        hipLaunchKernelGGL(combine_kernel<kBF16>, grid, block, 0, s, y2, weights, T, H, top_k, o);
+    } else {
+        hipLaunchKernelGGL(combine_kernel<kF16>, grid, block, 0, s, y2, weights, T, H, top_k, o);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -1,0 +1,447 @@
+// qmoe_api.cpp -- the C ABI of libqmoe.so: argument validation, workspace
+// layout, path selection and launches.  Every check runs before the first
+// launch, so an error return leaves the stream and all outputs untouched
+// [qmoe.rs, QMoEKernel::execute validates every input before launching and
+// returns early for zero rows; its checked_product / checked_bytes guard
+// size arithmetic].
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "qmoe.h"
+#include "qmoe_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = std::string("qmoe: ") + buf;
+    return code;
+}
+
+int ok()
+{
+    g_error.clear();
+    return QMOE_OK;
+}
+
+int hip_fail(hipError_t e, const char* what)
+{
+    return fail(QMOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------- kernel timer
+struct Timer {
+    std::mutex mu;
+    int stage = -1;
+    std::vector<hipEvent_t> start, stop;
+    size_t used = 0;
+};
+Timer g_timer;
+constexpr size_t kTimerPairs = 4096;
+
+void timer_begin(int stage, hipStream_t s)
+{
+    if (g_timer.stage == stage && g_timer.used < g_timer.start.size()) {
+        (void)hipEventRecord(g_timer.start[g_timer.used], s);
+    }
+}
+
+void timer_end(int stage, hipStream_t s)
+{
+    if (g_timer.stage == stage && g_timer.used < g_timer.start.size()) {
+        (void)hipEventRecord(g_timer.stop[g_timer.used], s);
+        ++g_timer.used;
+    }
+}
+
+// ---------------------------------------------------------------- workspace
+constexpr size_t kAlign = 256;
+
+struct Layout {
+    bool decode;
+    int m_tile;
+    int nt1, nt2;       // n-tiles of fc1 (activation columns) and fc2 (hidden columns)
+    int64_t cap1, cap2;  // work-list capacities
+    size_t ids, w, offsets, sorted, wl1, n1, wl2, n2, act, y2, total;
+};
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L)
+{
+    int64_t R;
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || top_k <= 0 || !mul_ok(T, top_k, &R) ||
+        R > INT32_MAX) {
+        return false;
+    }
+    L->decode = R <= QMOE_DECODE_MAX_ROUTES;
+    L->m_tile = L->decode ? qmoe::kDecodeMT : qmoe::kPrefillMT;
+    const int fc1_cols = L->decode ? qmoe::kDecodeFc1Cols : qmoe::kPrefillFc1Cols;
+    const int fc2_cols = L->decode ? qmoe::kDecodeFc2Cols : qmoe::kPrefillFc2Cols;
+    L->nt1 = (int)ceil_div(I, fc1_cols);
+    L->nt2 = (int)ceil_div(H, fc2_cols);
+    const int64_t m_tiles = ceil_div(R, L->m_tile) + (E < R ? E : R);
+    if (!mul_ok(m_tiles, L->nt1, &L->cap1) || !mul_ok(m_tiles, L->nt2, &L->cap2) ||
+        L->cap1 > INT32_MAX || L->cap2 > INT32_MAX) {
+        return false;
+    }
+    int64_t act_bytes, y2_bytes;
+    if (!mul_ok(R, (int64_t)I * 2, &act_bytes) || !mul_ok(R, (int64_t)H * 4, &y2_bytes)) {
+        return false;
+    }
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + (bytes ? bytes : 1));
+        return at;
+    };
+    L->ids = take((size_t)R * 4);
+    L->w = take((size_t)R * 4);
+    L->offsets = take(((size_t)E + 1) * 4);
+    L->sorted = take((size_t)R * 4);
+    L->wl1 = take((size_t)(L->cap1 > 0 ? L->cap1 : 1) * 12);
+    L->n1 = take(4);
+    L->wl2 = take((size_t)(L->cap2 > 0 ? L->cap2 : 1) * 12);
+    L->n2 = take(4);
+    L->act = take((size_t)act_bytes);
+    L->y2 = take((size_t)y2_bytes);
+    L->total = off;
+    return true;
+}
+
+int check_bits(const char* name, int bits)
+{
+    if (bits == 2 || bits == 3 || bits == 4) return QMOE_OK;
+    if (bits == 1 || bits == 8) {
+        return fail(QMOE_ERR_UNSUPPORTED, "%s bits=%d: only 2, 3 and 4 have kernels", name, bits);
+    }
+    return fail(QMOE_ERR_INVALID_ARG, "%s bits=%d is not a weight width", name, bits);
+}
+
+int check_proj(const char* name, const qmoe_proj* p)
+{
+    if (!p) return fail(QMOE_ERR_INVALID_ARG, "%s is NULL", name);
+    const int rc = check_bits(name, p->bits);
+    if (rc) return rc;
+    if (!p->codes || !p->scales) return fail(QMOE_ERR_INVALID_ARG, "%s codes/scales is NULL", name);
+    if (!aligned(p->codes, 16)) return fail(QMOE_ERR_INVALID_ARG, "%s codes not 16-byte aligned", name);
+    if (!aligned(p->scales, 2)) return fail(QMOE_ERR_INVALID_ARG, "%s scales not 2-byte aligned", name);
+    return QMOE_OK;
+}
+
+qmoe::ProjArgs proj_args(const qmoe_proj* p, float zpo)
+{
+    qmoe::ProjArgs a;
+    a.codes = p->codes;
+    a.scales = p->scales;
+    a.zp = p->zero_points;
+    a.bits = p->bits;
+    a.zp_fallback = p->zero_points ? 0.0f
+                    : std::isnan(zpo) ? (float)(1 << (p->bits - 1))
+                                      : zpo;
+    return a;
+}
+
+int check_zpo(float zpo)
+{
+    if (std::isinf(zpo)) return fail(QMOE_ERR_INVALID_ARG, "zero_point_offset must be finite or NaN");
+    return QMOE_OK;
+}
+
+int check_block_size(int bs)
+{
+    if (bs < 16 || !is_pow2(bs)) {
+        return fail(QMOE_ERR_INVALID_ARG, "block_size=%d must be a power of two >= 16", bs);
+    }
+    return QMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qmoe_last_error(void) { return g_error.c_str(); }
+
+int qmoe_route(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t normalize,
+               int32_t* topk_ids, float* topk_weights, void* stream)
+{
+    if (T < 0) return fail(QMOE_ERR_INVALID_ARG, "T=%lld < 0", (long long)T);
+    if (E < 1 || E > 1024) return fail(QMOE_ERR_INVALID_ARG, "E=%d outside [1, 1024]", E);
+    if (top_k < 1 || top_k > E) return fail(QMOE_ERR_INVALID_ARG, "top_k=%d outside [1, E=%d]", top_k, E);
+    if (normalize != 0 && normalize != 1) return fail(QMOE_ERR_INVALID_ARG, "normalize must be 0 or 1");
+    int64_t n;
+    if (!mul_ok(T, E, &n) || !mul_ok(T, top_k, &n)) return fail(QMOE_ERR_INVALID_ARG, "T*E overflows");
+    if (T == 0) return ok();
+    if (!logits || !topk_ids || !topk_weights) return fail(QMOE_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4)) {
+        return fail(QMOE_ERR_INVALID_ARG, "misaligned pointer");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    timer_begin(QMOE_STAGE_ROUTE, s);
+    const hipError_t e = qmoe::launch_route(logits, T, E, top_k, normalize, topk_ids, topk_weights, s);
+    timer_end(QMOE_STAGE_ROUTE, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "route launch");
+}
+
+int64_t qmoe_worklist_capacity(int64_t T, int32_t top_k, int32_t E, int32_t m_tile,
+                               int32_t n_tile, int32_t N)
+{
+    int64_t R, cap;
+    if (T < 0 || top_k < 1 || E < 1 || m_tile < 1 || n_tile < 1 || N < 1 || !mul_ok(T, top_k, &R)) {
+        return -1;
+    }
+    const int64_t m_tiles = ceil_div(R, m_tile) + (E < R ? E : R);
+    if (!mul_ok(m_tiles, ceil_div(N, n_tile), &cap)) return -1;
+    return cap;
+}
+
+int qmoe_group(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int32_t m_tile,
+               int32_t n_tile, int32_t N, int32_t* expert_offsets, int32_t* sorted_routes,
+               int32_t* worklist, int64_t worklist_capacity, int32_t* n_items, void* stream)
+{
+    if (T < 0 || top_k < 1) return fail(QMOE_ERR_INVALID_ARG, "T=%lld, top_k=%d", (long long)T, top_k);
+    if (E < 1 || E > 1024) return fail(QMOE_ERR_INVALID_ARG, "E=%d outside [1, 1024]", E);
+    if (m_tile < 1 || n_tile < 1 || N < 1) return fail(QMOE_ERR_INVALID_ARG, "m_tile, n_tile, N must be >= 1");
+    int64_t R;
+    if (!mul_ok(T, top_k, &R) || R > INT32_MAX) return fail(QMOE_ERR_INVALID_ARG, "T*top_k must be < 2^31");
+    const int64_t need = qmoe_worklist_capacity(T, top_k, E, m_tile, n_tile, N);
+    if (need < 0 || need > INT32_MAX) return fail(QMOE_ERR_INVALID_ARG, "work-list size overflows");
+    if (worklist_capacity < need) {
+        return fail(QMOE_ERR_WORKSPACE, "worklist_capacity=%lld < %lld", (long long)worklist_capacity,
+                    (long long)need);
+    }
+    if (!expert_offsets || !n_items || !worklist || (R > 0 && (!topk_ids || !sorted_routes))) {
+        return fail(QMOE_ERR_INVALID_ARG, "NULL pointer");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    timer_begin(QMOE_STAGE_GROUP, s);
+    const hipError_t e = qmoe::launch_group(topk_ids, (int)R, E, m_tile, (int)ceil_div(N, n_tile),
+                                            expert_offsets, sorted_routes, worklist,
+                                            worklist_capacity, n_items, 0, nullptr, 0, nullptr, s);
+    timer_end(QMOE_STAGE_GROUP, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "group launch");
+}
+
+size_t qmoe_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t top_k, int32_t dtype)
+{
+    Layout L;
+    if ((dtype != QMOE_DTYPE_F16 && dtype != QMOE_DTYPE_BF16) || !make_layout(T, H, I, E, top_k, &L)) {
+        return 0;
+    }
+    return L.total;
+}
+
+int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, int32_t I,
+                 int32_t E, const qmoe_proj* fc1, const qmoe_proj* fc2, float zero_point_offset,
+                 int32_t block_size, int32_t top_k, int32_t normalize, int32_t activation,
+                 int32_t dtype, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                 void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc;
+    if (T < 0) return fail(QMOE_ERR_INVALID_ARG, "T=%lld < 0", (long long)T);
+    if (H <= 0 || I <= 0) return fail(QMOE_ERR_INVALID_ARG, "H=%d and I=%d must be > 0", H, I);
+    if (E < 1 || E > 1024) return fail(QMOE_ERR_INVALID_ARG, "E=%d outside [1, 1024]", E);
+    if (top_k < 1 || top_k > E) return fail(QMOE_ERR_INVALID_ARG, "top_k=%d outside [1, E=%d]", top_k, E);
+    if (normalize != 0 && normalize != 1) return fail(QMOE_ERR_INVALID_ARG, "normalize must be 0 or 1");
+    if (activation != QMOE_ACT_SWIGLU && activation != QMOE_ACT_GEGLU) {
+        return fail(QMOE_ERR_INVALID_ARG, "activation=%d is neither SWIGLU (0) nor GEGLU (1)", activation);
+    }
+    if (dtype != QMOE_DTYPE_F16 && dtype != QMOE_DTYPE_BF16) {
+        return fail(QMOE_ERR_INVALID_ARG, "dtype=%d is neither F16 (1) nor BF16 (2)", dtype);
+    }
+    if ((rc = check_block_size(block_size))) return rc;
+    if (H % block_size || I % block_size) {
+        return fail(QMOE_ERR_INVALID_ARG, "H=%d and I=%d must be multiples of block_size=%d", H, I,
+                    block_size);
+    }
+    if ((rc = check_proj("fc1", fc1)) || (rc = check_proj("fc2", fc2))) return rc;
+    if ((rc = check_zpo(zero_point_offset))) return rc;
+    if (H % qmoe::kSuperK || I % qmoe::kSuperK) {
+        return fail(QMOE_ERR_UNSUPPORTED, "H=%d and I=%d must be multiples of %d", H, I, qmoe::kSuperK);
+    }
+    Layout L;
+    if (!make_layout(T, H, I, E, top_k, &L)) return fail(QMOE_ERR_INVALID_ARG, "sizes overflow");
+    if (T == 0) return ok();
+    if (!hidden || !logits || !out) return fail(QMOE_ERR_INVALID_ARG, "hidden, logits and out must be non-NULL");
+    if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(logits, 4)) {
+        return fail(QMOE_ERR_INVALID_ARG, "hidden/out must be 16-byte and logits 4-byte aligned");
+    }
+    if ((topk_ids_out && !aligned(topk_ids_out, 4)) || (topk_w_out && !aligned(topk_w_out, 4))) {
+        return fail(QMOE_ERR_INVALID_ARG, "misaligned routing output");
+    }
+    if (!workspace || !aligned(workspace, kAlign)) {
+        return fail(QMOE_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
+    }
+    if (workspace_bytes < L.total) {
+        return fail(QMOE_ERR_WORKSPACE, "workspace_bytes=%zu < %zu", workspace_bytes, L.total);
+    }
+
+    const int64_t R = T * top_k;
+    char* ws = static_cast<char*>(workspace);
+    int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
+    float* w = reinterpret_cast<float*>(ws + L.w);
+    int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+    int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+    int32_t* wl1 = reinterpret_cast<int32_t*>(ws + L.wl1);
+    int32_t* n1 = reinterpret_cast<int32_t*>(ws + L.n1);
+    int32_t* wl2 = reinterpret_cast<int32_t*>(ws + L.wl2);
+    int32_t* n2 = reinterpret_cast<int32_t*>(ws + L.n2);
+    void* act = ws + L.act;
+    float* y2 = reinterpret_cast<float*>(ws + L.y2);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+
+    timer_begin(QMOE_STAGE_ROUTE, s);
+    e = qmoe::launch_route(logits, T, E, top_k, normalize, ids, w, s);
+    timer_end(QMOE_STAGE_ROUTE, s);
+    if (e != hipSuccess) return hip_fail(e, "route launch");
+
+    timer_begin(QMOE_STAGE_GROUP, s);
+    e = qmoe::launch_group(ids, (int)R, E, L.m_tile, L.nt1, offsets, sorted, wl1, L.cap1, n1, L.nt2,
+                           wl2, L.cap2, n2, s);
+    timer_end(QMOE_STAGE_GROUP, s);
+    if (e != hipSuccess) return hip_fail(e, "group launch");
+
+    qmoe::ProjLaunch p1{};
+    p1.a = hidden;
+    p1.w = proj_args(fc1, zero_point_offset);
+    p1.K = H;
+    p1.N = 2 * I;
+    p1.block_size = block_size;
+    p1.top_k = top_k;
+    p1.offsets = offsets;
+    p1.sorted = sorted;
+    p1.worklist = wl1;
+    p1.n_items = n1;
+    p1.grid = L.cap1 > 0 ? L.cap1 : 1;
+    p1.act = activation;
+    p1.act_out = act;
+    timer_begin(QMOE_STAGE_FC1, s);
+    e = L.decode ? qmoe::launch_fc1_decode(p1, dtype, s) : qmoe::launch_fc1_prefill(p1, dtype, s);
+    timer_end(QMOE_STAGE_FC1, s);
+    if (e != hipSuccess) return hip_fail(e, "fc1 launch");
+
+    qmoe::ProjLaunch p2{};
+    p2.a = act;
+    p2.w = proj_args(fc2, zero_point_offset);
+    p2.K = I;
+    p2.N = H;
+    p2.block_size = block_size;
+    p2.top_k = top_k;
+    p2.offsets = offsets;
+    p2.sorted = sorted;
+    p2.worklist = wl2;
+    p2.n_items = n2;
+    p2.grid = L.cap2 > 0 ? L.cap2 : 1;
+    p2.y2 = y2;
+    timer_begin(QMOE_STAGE_FC2, s);
+    e = L.decode ? qmoe::launch_fc2_decode(p2, dtype, s) : qmoe::launch_fc2_prefill(p2, dtype, s);
+    timer_end(QMOE_STAGE_FC2, s);
+    if (e != hipSuccess) return hip_fail(e, "fc2 launch");
+
+    timer_begin(QMOE_STAGE_COMBINE, s);
+    e = qmoe::launch_combine(y2, w, T, H, top_k, out, dtype, s);
+    timer_end(QMOE_STAGE_COMBINE, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+
+    if (topk_ids_out) {
+        e = hipMemcpyAsync(topk_ids_out, ids, (size_t)R * 4, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "copy topk_ids");
+    }
+    if (topk_w_out) {
+        e = hipMemcpyAsync(topk_w_out, w, (size_t)R * 4, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "copy topk_weights");
+    }
+    return ok();
+}
+
+int qmoe_dequantize(const qmoe_proj* p, int32_t E, int32_t N, int32_t K, int32_t block_size,
+                    float zero_point_offset, int32_t dtype, int32_t* codes_out, void* w_out,
+                    void* stream)
+{
+    int rc;
+    if ((rc = check_proj("projection", p))) return rc;
+    if (E < 1 || N < 1 || K < 1) return fail(QMOE_ERR_INVALID_ARG, "E, N, K must be >= 1");
+    if ((rc = check_block_size(block_size))) return rc;
+    if (K % block_size) return fail(QMOE_ERR_INVALID_ARG, "K=%d not a multiple of block_size", K);
+    if (K % 32) return fail(QMOE_ERR_UNSUPPORTED, "K=%d must be a multiple of 32", K);
+    if (dtype != QMOE_DTYPE_F16 && dtype != QMOE_DTYPE_BF16) return fail(QMOE_ERR_INVALID_ARG, "bad dtype");
+    if ((rc = check_zpo(zero_point_offset))) return rc;
+    if (!w_out || !aligned(w_out, 16) || (codes_out && !aligned(codes_out, 4))) {
+        return fail(QMOE_ERR_INVALID_ARG, "w_out must be non-NULL and 16-byte aligned");
+    }
+    int64_t rows, elems;
+    if (!mul_ok(E, N, &rows) || !mul_ok(rows, K, &elems)) return fail(QMOE_ERR_INVALID_ARG, "size overflow");
+    hipStream_t s = (hipStream_t)stream;
+    const hipError_t e = qmoe::launch_dequant(proj_args(p, zero_point_offset), rows, K, block_size,
+                                              dtype, codes_out, w_out, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "dequant launch");
+}
+
+int qmoe_timer_start(int32_t stage)
+{
+    if (stage < QMOE_STAGE_ROUTE || stage > QMOE_STAGE_COMBINE) {
+        return fail(QMOE_ERR_INVALID_ARG, "unknown stage %d", stage);
+    }
+    std::lock_guard<std::mutex> lock(g_timer.mu);
+    if (g_timer.start.empty()) {
+        g_timer.start.resize(kTimerPairs);
+        g_timer.stop.resize(kTimerPairs);
+        for (size_t i = 0; i < kTimerPairs; ++i) {
+            hipError_t e = hipEventCreate(&g_timer.start[i]);
+            if (e == hipSuccess) e = hipEventCreate(&g_timer.stop[i]);
+            if (e != hipSuccess) {
+                g_timer.start.clear();
+                g_timer.stop.clear();
+                return hip_fail(e, "timer event create");
+            }
+        }
+    }
+    g_timer.used = 0;
+    g_timer.stage = stage;
+    return ok();
+}
+
+int qmoe_timer_stop(double* total_ms, int64_t* launches)
+{
+    std::lock_guard<std::mutex> lock(g_timer.mu);
+    double sum = 0.0;
+    for (size_t i = 0; i < g_timer.used; ++i) {
+        float ms = 0.0f;
+        hipError_t e = hipEventSynchronize(g_timer.stop[i]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, g_timer.start[i], g_timer.stop[i]);
+        if (e != hipSuccess) {
+            g_timer.stage = -1;
+            return hip_fail(e, "timer read");
+        }
+        sum += ms;
+    }
+    if (total_ms) *total_ms = sum;
+    if (launches) *launches = (int64_t)g_timer.used;
+    g_timer.stage = -1;
+    g_timer.used = 0;
+    return ok();
+}
+
+}  // extern "C"

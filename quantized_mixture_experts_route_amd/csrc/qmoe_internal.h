@@ -1,0 +1,71 @@
+// qmoe_internal.h -- host-side launch interface between the C ABI layer
+// (qmoe_api.cpp) and the kernel translation units.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+// Tile shapes.  Prefill: a workgroup computes kPrefillMT routed rows of one
+// expert against 256 weight rows (4 waves x 4 MFMA column blocks of 16).
+// Decode: a workgroup computes up to 16 rows against 64 weight rows, its 4
+// waves splitting K.
+constexpr int kPrefillMT = 128;
+constexpr int kPrefillWeightRows = 256;
+constexpr int kDecodeMT = 16;
+constexpr int kDecodeWeightRows = 64;
+constexpr int kSuperK = 128;  // inputs per K super-step: 4 lane groups x 32 codes
+
+// Output columns one work-list item covers (fc1 counts activation columns,
+// i.e. gate/up row pairs; fc2 counts hidden columns).
+constexpr int kPrefillFc1Cols = kPrefillWeightRows / 2;
+constexpr int kPrefillFc2Cols = kPrefillWeightRows;
+constexpr int kDecodeFc1Cols = kDecodeWeightRows / 2;
+constexpr int kDecodeFc2Cols = kDecodeWeightRows;
+
+struct ProjArgs {
+    const uint8_t* codes;
+    const void* scales;
+    const uint8_t* zp;  // nullable
+    float zp_fallback;  // fractional offset or symmetric centre
+    int bits;
+};
+
+// One grouped projection over a work-list.
+struct ProjLaunch {
+    const void* a;            // fc1: hidden [T, K]; fc2: activations [R, K] in sorted order
+    ProjArgs w;
+    int K;                    // inputs
+    int N;                    // weight rows (fc1: 2*I, fc2: H)
+    int block_size;
+    int top_k;
+    const int32_t* offsets;   // [E+1]
+    const int32_t* sorted;    // [R]
+    const int32_t* worklist;  // [cap, 3]
+    const int32_t* n_items;   // [1]
+    int64_t grid;             // workgroups to launch (>= 1)
+    int act;                  // fc1 only
+    void* act_out;            // fc1: dtype [R, I] in sorted order
+    float* y2;                // fc2: float32 [R, H] by route id
+};
+
+hipError_t launch_route(const float* logits, int64_t T, int E, int top_k, int normalize,
+                        int32_t* ids, float* weights, hipStream_t s);
+
+hipError_t launch_group(const int32_t* ids, int R, int E, int m_tile, int nt1, int32_t* offsets,
+                        int32_t* sorted, int32_t* wl1, int64_t cap1, int32_t* n1, int nt2,
+                        int32_t* wl2, int64_t cap2, int32_t* n2, hipStream_t s);
+
+hipError_t launch_fc1_prefill(const ProjLaunch& p, int dtype, hipStream_t s);
+hipError_t launch_fc2_prefill(const ProjLaunch& p, int dtype, hipStream_t s);
+hipError_t launch_fc1_decode(const ProjLaunch& p, int dtype, hipStream_t s);
+hipError_t launch_fc2_decode(const ProjLaunch& p, int dtype, hipStream_t s);
+
+hipError_t launch_combine(const float* y2, const float* weights, int64_t T, int H, int top_k,
+                          void* out, int dtype, hipStream_t s);
+
+hipError_t launch_dequant(const ProjArgs& w, int64_t rows, int K, int block_size, int dtype,
+                          int32_t* codes_out, void* w_out, hipStream_t s);
+
+}  // namespace qmoe

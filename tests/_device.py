@@ -1,0 +1,64 @@
+"""Helpers moving synthetic inputs onto the GPU and running the library on them."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import quantized_mixture_experts_route_amd as qm
+
+
+def torch_dtype(code: int) -> torch.dtype:
+    return torch.float16 if code == 1 else torch.bfloat16
+
+
+def bits_tensor(arr: np.ndarray, code: int, device="cuda") -> torch.Tensor:
+    """uint16 bit patterns -> fp16/bf16 device tensor (same bits)."""
+    t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16))
+    return t.view(torch_dtype(code)).to(device)
+
+
+def to_device(inp: dict, spec: dict, device="cuda") -> dict:
+    dt = spec["dtype"]
+    out = dict(hidden=bits_tensor(inp["hidden"], dt, device),
+               logits=torch.from_numpy(inp["logits"]).to(device))
+    for name in ("fc1", "fc2"):
+        zp = inp[name + "_zp"]
+        out[name] = qm.Projection(
+            codes=torch.from_numpy(inp[name + "_codes"]).to(device),
+            scales=bits_tensor(inp[name + "_scales"], dt, device),
+            zero_points=None if zp is None else torch.from_numpy(zp).to(device),
+            bits=spec[name + "_bits"])
+    return out
+
+
+def run_layer(dev: dict, spec: dict, **kw):
+    return qm.forward(dev["hidden"], dev["logits"], dev["fc1"], dev["fc2"], top_k=spec["k"],
+                      block_size=spec["block_size"], normalize=spec["normalize"],
+                      activation=spec["act"], zero_point_offset=spec["zpo"], **kw)
+
+
+def tolerance(ref: np.ndarray) -> float:
+    """Layer-output bound: 1e-2 * max|ref| + 1e-3."""
+    return 1e-2 * float(np.abs(ref).max()) + 1e-3
+
+
+def round_to_dtype_bits(x: np.ndarray, code: int) -> np.ndarray:
+    """Correctly rounded (nearest even) fp16/bf16 bit patterns of float64 values.
+
+    bf16 goes through float32, which is exact for the values used here
+    (asserted), so only one rounding happens."""
+    if code == 1:
+        return x.astype(np.float16).view(np.uint16)
+    x32 = x.astype(np.float32)
+    assert np.array_equal(x32.astype(np.float64), x), "value not exact in float32"
+    return torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def as_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def nan_to(x):
+    return math.nan if x is None else x

@@ -1,0 +1,178 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/qmoe.h declares, sizes its workspace, and rejects every invalid
+argument before touching the device (these calls never reach a launch)."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import quantized_mixture_experts_route_amd as qm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmoe.h")
+
+FAKE = 1 << 20  # a 256-byte aligned non-NULL address; never dereferenced on these paths
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(qmoe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_bound_entry_points():
+    assert set(_declared()) == set(qm.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qm.load_library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (QMOE_[A-Z0-9_]+) \(?(-?\d+)\)?", text))
+    assert int(consts["QMOE_OK"]) == qm.OK
+    assert int(consts["QMOE_ERR_INVALID_ARG"]) == qm.ERR_INVALID_ARG
+    assert int(consts["QMOE_ERR_UNSUPPORTED"]) == qm.ERR_UNSUPPORTED
+    assert int(consts["QMOE_ERR_WORKSPACE"]) == qm.ERR_WORKSPACE
+    assert int(consts["QMOE_ERR_HIP"]) == qm.ERR_HIP
+    assert int(consts["QMOE_DTYPE_F16"]) == qm.DTYPE_F16
+    assert int(consts["QMOE_DTYPE_BF16"]) == qm.DTYPE_BF16
+    assert int(consts["QMOE_ACT_SWIGLU"]) == qm.ACT_SWIGLU
+    assert int(consts["QMOE_ACT_GEGLU"]) == qm.ACT_GEGLU
+    assert int(consts["QMOE_DECODE_MAX_ROUTES"]) == qm.DECODE_MAX_ROUTES
+
+
+def test_worklist_capacity_formula():
+    # (ceil(R/m_tile) + min(E, R)) * ceil(N/n_tile)
+    assert qm.worklist_capacity(512, 2, 8, 128, 128, 2048) == (8 + 8) * 16
+    assert qm.worklist_capacity(6, 10, 512, 16, 32, 768) == (4 + 60) * 24
+    assert qm.worklist_capacity(0, 2, 8, 16, 16, 16) == 0
+    assert qm.worklist_capacity(-1, 2, 8, 16, 16, 16) == -1
+
+
+def test_workspace_size_monotone_and_invalid():
+    a = qm.workspace_size(8, 2048, 2048, 8, 2, 1)
+    b = qm.workspace_size(512, 2048, 2048, 8, 2, 1)
+    assert 0 < a < b
+    assert a % 256 == 0 and b % 256 == 0
+    # fp32 [R, H] plus dtype [R, I] intermediates dominate
+    assert b >= 1024 * 2048 * 4 + 1024 * 2048 * 2
+    assert qm.workspace_size(8, 2048, 2048, 8, 2, 3) == 0
+    assert qm.workspace_size(8, 0, 2048, 8, 2, 1) == 0
+    assert qm.workspace_size(1 << 40, 2048, 2048, 8, 2, 1) == 0
+
+
+def _proj(bits=4, codes=FAKE, scales=FAKE, zp=None):
+    return qm._Proj(codes, scales, zp, bits)
+
+
+def _fwd(lib, **kw):
+    args = dict(hidden=FAKE, logits=FAKE, T=4, H=256, I=256, E=8, fc1=_proj(), fc2=_proj(),
+                zpo=math.nan, bs=32, k=2, normalize=1, act=0, dtype=1, out=FAKE, ids=None,
+                w=None, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    fc1 = ctypes.byref(args["fc1"]) if args["fc1"] is not None else None
+    fc2 = ctypes.byref(args["fc2"]) if args["fc2"] is not None else None
+    return lib.qmoe_forward(args["hidden"], args["logits"], args["T"], args["H"], args["I"],
+                            args["E"], fc1, fc2, args["zpo"], args["bs"], args["k"],
+                            args["normalize"], args["act"], args["dtype"], args["out"],
+                            args["ids"], args["w"], args["ws"], args["ws_bytes"], None)
+
+
+INVALID_FORWARD = [
+    (dict(T=-1), qm.ERR_INVALID_ARG),
+    (dict(H=0), qm.ERR_INVALID_ARG),
+    (dict(E=0), qm.ERR_INVALID_ARG),
+    (dict(E=1025), qm.ERR_INVALID_ARG),
+    (dict(k=0), qm.ERR_INVALID_ARG),
+    (dict(k=9), qm.ERR_INVALID_ARG),
+    (dict(normalize=2), qm.ERR_INVALID_ARG),
+    (dict(act=2), qm.ERR_INVALID_ARG),
+    (dict(dtype=0), qm.ERR_INVALID_ARG),
+    (dict(bs=24), qm.ERR_INVALID_ARG),
+    (dict(bs=8), qm.ERR_INVALID_ARG),
+    (dict(H=272, bs=32), qm.ERR_INVALID_ARG),
+    (dict(H=160, bs=32), qm.ERR_UNSUPPORTED),
+    (dict(I=96, bs=32), qm.ERR_UNSUPPORTED),
+    (dict(fc1=_proj(bits=8)), qm.ERR_UNSUPPORTED),
+    (dict(fc2=_proj(bits=1)), qm.ERR_UNSUPPORTED),
+    (dict(fc2=_proj(bits=5)), qm.ERR_INVALID_ARG),
+    (dict(fc1=None), qm.ERR_INVALID_ARG),
+    (dict(fc1=_proj(codes=None)), qm.ERR_INVALID_ARG),
+    (dict(fc2=_proj(scales=None)), qm.ERR_INVALID_ARG),
+    (dict(fc1=_proj(codes=FAKE + 8)), qm.ERR_INVALID_ARG),
+    (dict(zpo=math.inf), qm.ERR_INVALID_ARG),
+    (dict(hidden=None), qm.ERR_INVALID_ARG),
+    (dict(out=FAKE + 2), qm.ERR_INVALID_ARG),
+    (dict(ws=None), qm.ERR_INVALID_ARG),
+    (dict(ws=FAKE + 64), qm.ERR_INVALID_ARG),
+    (dict(ws_bytes=1000), qm.ERR_WORKSPACE),
+    (dict(T=1 << 31), qm.ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,code", INVALID_FORWARD)
+def test_forward_rejects_before_launch(kw, code):
+    lib = qm.load_library()
+    rc = _fwd(lib, **kw)
+    assert rc == code, (kw, rc, qm.last_error())
+    assert qm.last_error().startswith("qmoe: ")
+
+
+def test_forward_zero_tokens_is_a_noop():
+    lib = qm.load_library()
+    # T = 0: every pointer of the token side may be NULL and nothing is launched
+    assert _fwd(lib, T=0, hidden=None, logits=None, out=None, ws=None, ws_bytes=0) == qm.OK
+    assert qm.last_error() == ""
+
+
+def test_route_validation():
+    lib = qm.load_library()
+    assert lib.qmoe_route(FAKE, 4, 0, 1, 1, FAKE, FAKE, None) == qm.ERR_INVALID_ARG
+    assert lib.qmoe_route(FAKE, 4, 8, 9, 1, FAKE, FAKE, None) == qm.ERR_INVALID_ARG
+    assert lib.qmoe_route(FAKE, 4, 8, 2, 3, FAKE, FAKE, None) == qm.ERR_INVALID_ARG
+    assert lib.qmoe_route(None, 4, 8, 2, 1, FAKE, FAKE, None) == qm.ERR_INVALID_ARG
+    assert lib.qmoe_route(FAKE + 1, 4, 8, 2, 1, FAKE, FAKE, None) == qm.ERR_INVALID_ARG
+    assert lib.qmoe_route(None, 0, 8, 2, 1, None, None, None) == qm.OK
+
+
+def test_group_validation():
+    lib = qm.load_library()
+    cap = qm.worklist_capacity(8, 2, 8, 16, 32, 64)
+    args = [FAKE, 8, 2, 8, 16, 32, 64, FAKE, FAKE, FAKE, cap, FAKE, None]
+    bad = list(args)
+    bad[10] = cap - 1
+    assert lib.qmoe_group(*bad) == qm.ERR_WORKSPACE
+    bad = list(args)
+    bad[3] = 2000
+    assert lib.qmoe_group(*bad) == qm.ERR_INVALID_ARG
+    bad = list(args)
+    bad[4] = 0
+    assert lib.qmoe_group(*bad) == qm.ERR_INVALID_ARG
+    bad = list(args)
+    bad[7] = None
+    assert lib.qmoe_group(*bad) == qm.ERR_INVALID_ARG
+
+
+def test_dequantize_validation():
+    lib = qm.load_library()
+    p = _proj(bits=3)
+    assert lib.qmoe_dequantize(ctypes.byref(p), 1, 1, 48, 16, math.nan, 1, None, FAKE, None) \
+        == qm.ERR_UNSUPPORTED
+    assert lib.qmoe_dequantize(ctypes.byref(p), 1, 1, 64, 48, math.nan, 1, None, FAKE, None) \
+        == qm.ERR_INVALID_ARG
+    assert lib.qmoe_dequantize(ctypes.byref(p), 1, 1, 64, 32, math.nan, 1, None, None, None) \
+        == qm.ERR_INVALID_ARG
+    assert lib.qmoe_dequantize(None, 1, 1, 64, 32, math.nan, 1, None, FAKE, None) \
+        == qm.ERR_INVALID_ARG
+
+
+def test_timer_validation():
+    lib = qm.load_library()
+    assert lib.qmoe_timer_start(7) == qm.ERR_INVALID_ARG
