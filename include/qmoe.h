@@ -53,8 +53,8 @@ extern "C" {
 #define QMOE_DTYPE_BF16 2
 
 /* gated activations on interleaved fc1 rows (row 2j = gate, 2j+1 = up)
- * [qmoe.rs, qmoe_activate with swiglu_fusion = 1; PR 32198, GeGLU "gated like
- * SwiGLU (interleaved fc1)"] */
+ * [qmoe.rs, qmoe_activate with swiglu_fusion = 1; PR 32198, GeGLU uses the same
+ * interleaved fc1 rows as SwiGLU with a tanh-GELU gate] */
 #define QMOE_ACT_SWIGLU 0 /* silu(g) * u                                            */
 #define QMOE_ACT_GEGLU 1  /* 0.5 g (1 + tanh(0.7978845608028654 (g + 0.044715 g^3))) * u */
 
