@@ -25,6 +25,8 @@ SOURCES = ["qmoe_api.cpp", "route.hip", "group.hip", "gemm_prefill.hip", "gemm_d
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          # packed fp32 VALU ops stay off: plain scalar fp32 everywhere
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in VGPRs: no accvgpr copies around every MFMA
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -1,57 +1,69 @@
 // dequant.hip -- the projections' dequantization written out to memory, as a
-// test hook.  It calls the same span load, group extraction, zero-point and
-// dequant8 routines the projection kernels use, one thread per 32-code span.
-#include "qmoe_device.h"
-#include "qmoe_internal.h"
+// test hook.  One thread per 32-code span calls the same span load, zero-point
+// and dequant_step / dequant_step_generic routines the projection kernels use,
+// then stores every value at its input position (undoing the register order
+// of code_order<DT, BITS>()).
+#include "gemm_common.h"
 
 namespace qmoe {
 namespace {
 
-template <int DT, int BITS>
+template <int DT, int BITS, int ZP>
 __global__ __launch_bounds__(256) void dequant_kernel(ProjArgs w, int64_t rows, int K,
                                                       int block_size, int32_t* codes_out,
                                                       uint16_t* w_out)
 {
+    constexpr Order O = code_order<DT, BITS>();
     const int spans = K / 32;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= rows * spans) return;
     const int64_t row = idx / spans;
     const int k0 = (int)(idx % spans) * 32;
-    const int n_blocks = K / block_size;
-    const uint8_t* codes = w.codes + row * (int64_t)(K * BITS / 8);
-    const uint16_t* scales = reinterpret_cast<const uint16_t*>(w.scales) + row * n_blocks;
-    const uint8_t* zp = w.zp ? w.zp + row * zp_row_bytes(n_blocks, BITS) : nullptr;
-    const Span<BITS> sp = load_span<BITS>(codes, k0);
+    const WeightRow r = weight_row(w, row, K, block_size);
+    const Span<BITS> sp = load_span<BITS>(r.codes, k0);
+    uint16_t* out = w_out + row * K + k0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int kk = k0 + 8 * i;
-        const int blk = kk / block_size;
-        const uint32_t group = span_group<BITS>(sp, i);
-        const u32x4 v = dequant8<DT, BITS>(group, zero_point<BITS>(zp, blk, w.zp_fallback),
-                                           Dt<DT>::to_float(scales[blk]));
-        *reinterpret_cast<u32x4*>(w_out + row * K + kk) = v;
-        if (codes_out) {
+    for (int t = 0; t < 4; ++t) {
+        // steps 0-1 and 2-3 each lie within one block (block_size >= 16)
+        const BlockParams q = decode_params<DT, BITS, ZP>(
+            load_params<ZP>(r, k0 + 16 * (t >> 1), block_size), w.zp_fallback);
+        const u32x4 v = dequant_zp<DT, BITS, ZP>(sp, t, q);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                codes_out[row * K + kk + j] = (int32_t)((group >> (BITS * j)) & ((1u << BITS) - 1u));
-            }
+        for (int i = 0; i < 4; ++i) {
+            out[order_lo(O, t, i)] = (uint16_t)(v[i] & 0xffffu);
+            out[order_hi(O, t, i)] = (uint16_t)(v[i] >> 16);
         }
     }
+    if (codes_out) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) codes_out[row * K + k0 + j] = (int32_t)span_code<BITS>(sp, j);
+    }
+}
+
+template <int DT, int BITS>
+hipError_t launch_zp(const ProjArgs& w, int64_t rows, int K, int block_size, int32_t* codes_out,
+                     uint16_t* w_out, hipStream_t s)
+{
+    const int64_t n = rows * (K / 32);
+    const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+    switch (zp_mode(w)) {
+    case kZpConst: hipLaunchKernelGGL((dequant_kernel<DT, BITS, kZpConst>), grid, block, 0, s, w, rows, K, block_size, codes_out, w_out); break;
+    case kZpTensor: hipLaunchKernelGGL((dequant_kernel<DT, BITS, kZpTensor>), grid, block, 0, s, w, rows, K, block_size, codes_out, w_out); break;
+    default: hipLaunchKernelGGL((dequant_kernel<DT, BITS, kZpGeneric>), grid, block, 0, s, w, rows, K, block_size, codes_out, w_out); break;
+    }
+    return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_dt(const ProjArgs& w, int64_t rows, int K, int block_size, int32_t* codes_out,
                      uint16_t* w_out, hipStream_t s)
 {
-    const int64_t n = rows * (K / 32);
-    const dim3 grid((unsigned)((n + 255) / 256)), block(256);
     switch (w.bits) {
-    case 2: hipLaunchKernelGGL((dequant_kernel<DT, 2>), grid, block, 0, s, w, rows, K, block_size, codes_out, w_out); break;
-    case 3: hipLaunchKernelGGL((dequant_kernel<DT, 3>), grid, block, 0, s, w, rows, K, block_size, codes_out, w_out); break;
-    case 4: hipLaunchKernelGGL((dequant_kernel<DT, 4>), grid, block, 0, s, w, rows, K, block_size, codes_out, w_out); break;
+    case 2: return launch_zp<DT, 2>(w, rows, K, block_size, codes_out, w_out, s);
+    case 3: return launch_zp<DT, 3>(w, rows, K, block_size, codes_out, w_out, s);
+    case 4: return launch_zp<DT, 4>(w, rows, K, block_size, codes_out, w_out, s);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace

@@ -7,9 +7,10 @@
 // those 32 positions are, as long as A and B use the same ones.  So within a
 // K super-step of 128 inputs, lane group g takes the 32 consecutive inputs
 // [32g, 32g+32) -- one contiguous span of packed codes per lane (16 B at
-// 4 bits) -- and MFMA step t (0..3) consumes inputs [32g+8t, 32g+8t+8).
-// The result block D[16x16] lands with lane l holding rows 4g..4g+3 of
-// column c.
+// 4 bits) -- and MFMA step t (0..3) consumes 8 of them in the register order
+// code_order<DT, BITS>() (qmoe_device.h); the A values are permuted to the
+// same order.  The result block D[16x16] lands with lane l holding rows
+// 4g..4g+3 of column c.
 #pragma once
 
 #include "qmoe_device.h"
@@ -21,6 +22,10 @@ struct WeightRow {
     const uint8_t* codes;
     const uint16_t* scales;
     const uint8_t* zp;  // nullable
+    int bits;
+
+    // byte of the zero-point row holding block blk's value
+    __device__ uint32_t zp_byte(int blk) const { return zp[bits == 3 ? blk : blk / (8 / bits)]; }
 };
 
 __device__ inline WeightRow weight_row(const ProjArgs& w, int64_t row, int K, int block_size)
@@ -30,18 +35,79 @@ __device__ inline WeightRow weight_row(const ProjArgs& w, int64_t row, int K, in
     r.codes = w.codes + row * (int64_t)(K * w.bits / 8);
     r.scales = reinterpret_cast<const uint16_t*>(w.scales) + row * n_blocks;
     r.zp = w.zp ? w.zp + row * zp_row_bytes(n_blocks, w.bits) : nullptr;
+    r.bits = w.bits;
     return r;
 }
 
-// B fragment for MFMA step t of a span whose step-t group starts at input kk.
-template <int DT, int BITS>
-__device__ inline u32x4 b_fragment(const Span<BITS>& sp, int t, int kk, const WeightRow& r,
-                                   float zp_fallback, int block_size)
+// Zero-point handling of a projection, fixed per launch:
+//   kZpConst   one zero point for every block (offset or centre), a multiple of
+//              1/2 below 256: fast dequant
+//   kZpTensor  per-block uint8 zero points (integers): fast dequant
+//   kZpGeneric one zero point of any other value: float32 dequant
+enum : int { kZpConst = 0, kZpTensor = 1, kZpGeneric = 2 };
+
+// Raw bits of one block's scale and packed zero point, loaded ahead of use so
+// that no load waits on another.
+struct RawParams {
+    uint32_t scale;
+    uint32_t zp;
+    int blk;
+};
+
+template <int ZP>
+__device__ inline RawParams load_params(const WeightRow& r, int kk, int block_size)
 {
-    const int blk = kk / block_size;
-    const float scale = Dt<DT>::to_float(r.scales[blk]);
-    const float zp = zero_point<BITS>(r.zp, blk, zp_fallback);
-    return dequant8<DT, BITS>(span_group<BITS>(sp, t), zp, scale);
+    RawParams q;
+    q.blk = kk / block_size;
+    q.scale = r.scales[q.blk];
+    q.zp = 0;
+    if constexpr (ZP == kZpTensor) q.zp = r.zp_byte(q.blk);
+    return q;
+}
+
+struct BlockParams {
+    float zp;
+    float scale;
+};
+
+template <int DT, int BITS, int ZP>
+__device__ inline BlockParams decode_params(const RawParams& q, float zp_const)
+{
+    BlockParams b;
+    b.scale = Dt<DT>::to_float((uint16_t)q.scale);
+    if constexpr (ZP == kZpTensor) {
+        if constexpr (BITS == 3) {
+            b.zp = (float)q.zp;
+        } else {
+            constexpr int per = 8 / BITS;
+            b.zp = (float)((q.zp >> ((q.blk % per) * BITS)) & ((1u << BITS) - 1u));
+        }
+    } else {
+        b.zp = zp_const;
+    }
+    return b;
+}
+
+template <int DT, int BITS, int ZP>
+__device__ inline u32x4 dequant_zp(const Span<BITS>& sp, int t, const BlockParams& b)
+{
+    if constexpr (ZP == kZpGeneric) return dequant_step_generic<DT, BITS>(sp, t, b.zp, b.scale);
+    else return dequant_step<DT, BITS>(sp, t, b.zp, b.scale);
+}
+
+inline int zp_mode(const ProjArgs& w)
+{
+    return w.zp ? kZpTensor : (w.fast ? kZpConst : kZpGeneric);
+}
+
+// 32 consecutive dtype values of an A row starting at element k (16-byte aligned).
+__device__ inline void load_a_span(const uint16_t* row, int k, uint32_t (&v)[16])
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(row + k + 8 * q);
+        v[4 * q + 0] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+    }
 }
 
 template <int DT>

@@ -6,7 +6,9 @@
 // item's rows.  Packed codes stream from HBM straight into registers, are
 // dequantized there as (code - zp) * scale and fed to bf16/fp16 MFMA; the
 // A rows (gathered hidden states for fc1, sorted activations for fc2) are
-// staged once per K super-step in LDS and shared by the four wavefronts.
+// staged per K super-step in a double-buffered LDS tile shared by the four
+// wavefronts, already permuted to the MFMA register order, while the next
+// super-step's A rows and packed spans are in flight.
 // [PR 32198: weights stay packed in HBM and are dequantized in registers
 // inside the GEMM; gemm_quant_moe.rs, moe_fp8_grouped_gemm: workgroups stride
 // over a compacted work-list, rows addressed through sorted route ids.]
@@ -23,13 +25,15 @@ namespace qmoe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLda = kSuperK + 8;  // LDS row pitch in 16-bit elements
+constexpr int kPitch = kSuperK / 2 + 4;  // LDS row pitch in 32-bit words (64 data + 4 pad)
 
-template <int DT, int BITS, bool FC1, int MT>
+template <int DT, int BITS, bool FC1, int MT, int ZP>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(ProjLaunch p)
 {
+    constexpr Order O = code_order<DT, BITS>();
     constexpr int MB = MT / 16;
-    __shared__ __attribute__((aligned(16))) uint16_t a_lds[MT * kLda];
+    constexpr int kChunks = MT * 4 / kThreads;  // (row, lane-group span) pieces staged per thread
+    __shared__ __attribute__((aligned(16))) uint32_t a_lds[2][MT * kPitch];
     __shared__ int row_src[MT];
 
     const int tid = threadIdx.x;
@@ -38,7 +42,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(ProjLaunch p)
     const int g = lane >> 4;
     const int c = lane & 15;
     const int K = p.K;
+    const int n_super = K / kSuperK;
     const int n_items = *p.n_items;
+    const bool two_blocks = p.block_size < 32;
     const uint16_t* a_src = reinterpret_cast<const uint16_t*>(p.a);
 
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -50,24 +56,23 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(ProjLaunch p)
 
         int col0;  // fc1: first activation column of this wave; fc2: first hidden column
         bool active;
-        int64_t wrow[4];
+        WeightRow wr[4];
         if constexpr (FC1) {
             col0 = nt * kPrefillFc1Cols + wave * 32;
             active = col0 < p.N / 2;
-            wrow[0] = 2 * (col0 + c);
-            wrow[1] = 2 * (col0 + c) + 1;
-            wrow[2] = 2 * (col0 + 16 + c);
-            wrow[3] = 2 * (col0 + 16 + c) + 1;
+            const int64_t base = (int64_t)e * p.N + (active ? 2 * (col0 + c) : 0);
+            wr[0] = weight_row(p.w, base, K, p.block_size);
+            wr[1] = weight_row(p.w, base + 1, K, p.block_size);
+            wr[2] = weight_row(p.w, base + (active ? 32 : 0), K, p.block_size);
+            wr[3] = weight_row(p.w, base + (active ? 33 : 1), K, p.block_size);
         } else {
             col0 = nt * kPrefillFc2Cols + wave * 64;
             active = col0 < p.N;
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) wrow[nb] = col0 + nb * 16 + c;
-        }
-        WeightRow wr[4];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            wr[nb] = weight_row(p.w, (int64_t)e * p.N + (active ? wrow[nb] : 0), K, p.block_size);
+            for (int nb = 0; nb < 4; ++nb) {
+                wr[nb] = weight_row(p.w, (int64_t)e * p.N + (active ? col0 + nb * 16 + c : 0), K,
+                                    p.block_size);
+            }
         }
 
         __syncthreads();  // the previous item is done with row_src and a_lds
@@ -78,45 +83,80 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(ProjLaunch p)
         }
         __syncthreads();
 
+        uint32_t a_stage[kChunks][16];
+        Span<BITS> sp[4];
+        RawParams bp[4];
+        auto load_step = [&](int s) {
+            const int k0 = s * kSuperK;
+#pragma unroll
+            for (int j = 0; j < kChunks; ++j) {
+                const int q = tid + kThreads * j;
+                const int src = row_src[q >> 2];
+                if (src >= 0) {
+                    load_a_span(a_src + (int64_t)src * K, k0 + 32 * (q & 3), a_stage[j]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) a_stage[j][i] = 0u;
+                }
+            }
+            if (active) {
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    sp[nb] = load_span<BITS>(wr[nb].codes, k0 + 32 * g);
+                    bp[nb] = load_params<ZP>(wr[nb], k0 + 32 * g, p.block_size);
+                }
+            }
+        };
+
         f32x4 acc[MB][4];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        for (int k0 = 0; k0 < K; k0 += kSuperK) {
+        load_step(0);
+        for (int s = 0; s < n_super; ++s) {
+            uint32_t* buf = a_lds[s & 1];
 #pragma unroll
-            for (int q = tid; q < MT * 16; q += kThreads) {
-                const int i = q >> 4;
-                const int ch = q & 15;
-                const int src = row_src[i];
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (src >= 0) {
-                    v = *reinterpret_cast<const u32x4*>(a_src + (int64_t)src * K + k0 + ch * 8);
+            for (int j = 0; j < kChunks; ++j) {
+                const int q = tid + kThreads * j;
+                uint32_t perm[16];
+                permute_span<O>(a_stage[j], perm);
+                uint32_t* dst = buf + (q >> 2) * kPitch + 16 * (q & 3);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    *reinterpret_cast<u32x4*>(dst + 4 * v) =
+                        u32x4{perm[4 * v], perm[4 * v + 1], perm[4 * v + 2], perm[4 * v + 3]};
                 }
-                *reinterpret_cast<u32x4*>(&a_lds[i * kLda + ch * 8]) = v;
             }
-            Span<BITS> sp[4];
-            if (active) {
+            Span<BITS> cur[4];
+            RawParams cbp[4];
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) sp[nb] = load_span<BITS>(wr[nb].codes, k0 + 32 * g);
+            for (int nb = 0; nb < 4; ++nb) {
+                cur[nb] = sp[nb];
+                cbp[nb] = bp[nb];
             }
             __syncthreads();
+            if (s + 1 < n_super) load_step(s + 1);  // in flight during the MFMAs below
+
             if (active) {
+                const int kk = s * kSuperK + 32 * g;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const int kk = k0 + 32 * g + 8 * t;
                     u32x4 bf[4];
 #pragma unroll
                     for (int nb = 0; nb < 4; ++nb) {
-                        bf[nb] = b_fragment<DT, BITS>(sp[nb], t, kk, wr[nb], p.w.zp_fallback,
-                                                      p.block_size);
+                        const RawParams rq = (two_blocks && t >= 2)
+                                                 ? load_params<ZP>(wr[nb], kk + 16, p.block_size)
+                                                 : cbp[nb];
+                        const BlockParams q = decode_params<DT, BITS, ZP>(rq, p.w.zp_fallback);
+                        bf[nb] = dequant_zp<DT, BITS, ZP>(cur[nb], t, q);
                     }
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) {
                         if (mb * 16 < rows) {
                             const u32x4 af = *reinterpret_cast<const u32x4*>(
-                                &a_lds[(mb * 16 + c) * kLda + 32 * g + 8 * t]);
+                                buf + (mb * 16 + c) * kPitch + 16 * g + 4 * t);
 #pragma unroll
                             for (int nb = 0; nb < 4; ++nb) {
                                 acc[mb][nb] = Dt<DT>::mfma(af, bf[nb], acc[mb][nb]);
@@ -125,7 +165,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(ProjLaunch p)
                     }
                 }
             }
-            __syncthreads();
         }
 
         if (!active) continue;
@@ -151,17 +190,28 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(ProjLaunch p)
     }
 }
 
+template <bool FC1, int DT, int BITS>
+hipError_t launch_zp(const ProjLaunch& p, hipStream_t s)
+{
+    const dim3 grid((unsigned)p.grid), block(kThreads);
+    constexpr int MT = kPrefillMT;
+    switch (zp_mode(p.w)) {
+    case kZpConst: hipLaunchKernelGGL((prefill_kernel<DT, BITS, FC1, MT, kZpConst>), grid, block, 0, s, p); break;
+    case kZpTensor: hipLaunchKernelGGL((prefill_kernel<DT, BITS, FC1, MT, kZpTensor>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((prefill_kernel<DT, BITS, FC1, MT, kZpGeneric>), grid, block, 0, s, p); break;
+    }
+    return hipGetLastError();
+}
+
 template <bool FC1, int DT>
 hipError_t launch_dt(const ProjLaunch& p, hipStream_t s)
 {
-    const dim3 grid((unsigned)p.grid), block(kThreads);
     switch (p.w.bits) {
-    case 2: hipLaunchKernelGGL((prefill_kernel<DT, 2, FC1, kPrefillMT>), grid, block, 0, s, p); break;
-    case 3: hipLaunchKernelGGL((prefill_kernel<DT, 3, FC1, kPrefillMT>), grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<DT, 4, FC1, kPrefillMT>), grid, block, 0, s, p); break;
+    case 2: return launch_zp<FC1, DT, 2>(p, s);
+    case 3: return launch_zp<FC1, DT, 3>(p, s);
+    case 4: return launch_zp<FC1, DT, 4>(p, s);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace

@@ -119,7 +119,7 @@ bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L)
     L->ids = take((size_t)R * 4);
     L->w = take((size_t)R * 4);
     L->offsets = take(((size_t)E + 1) * 4);
-    L->sorted = take((size_t)R * 4);
+    L->sorted = take(((size_t)R + qmoe::kDecodeMT) * 4);  // slack: decode reads 16 ids per item
     L->wl1 = take((size_t)(L->cap1 > 0 ? L->cap1 : 1) * 12);
     L->n1 = take(4);
     L->wl2 = take((size_t)(L->cap2 > 0 ? L->cap2 : 1) * 12);
@@ -160,6 +160,10 @@ qmoe::ProjArgs proj_args(const qmoe_proj* p, float zpo)
     a.zp_fallback = p->zero_points ? 0.0f
                     : std::isnan(zpo) ? (float)(1 << (p->bits - 1))
                                       : zpo;
+    // tensor zero points are integers; an offset must be a multiple of 1/2
+    const float twice = a.zp_fallback * 2.0f;
+    a.fast = p->zero_points != nullptr ||
+             (twice == std::floor(twice) && a.zp_fallback > -256.0f && a.zp_fallback < 256.0f);
     return a;
 }
 

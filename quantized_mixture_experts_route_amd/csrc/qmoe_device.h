@@ -146,23 +146,263 @@ __device__ inline float zero_point(const uint8_t* zp_row, int block, float fallb
     }
 }
 
-// ---------------------------------------------------------------- dequant
-// Eight codes -> eight dtype values (code - zp) * scale, each rounded once to
-// the dtype.  (code - zp) and its product with a 16-bit scale are exact in
-// float32 for integer or half-integer zero points, so the result is the
-// correctly rounded dequantized weight [PR 33569: dequantized weights are
-// rounded to the activation type before accumulation].
+// ---------------------------------------------------------------- code order
+// A 32-code span feeds four MFMA steps t = 0..3; each step takes 8 codes as
+// four registers r of two 16-bit values.  A contraction is indifferent to
+// which span codes go into which register as long as the A operand pairs the
+// same inputs, so each (dtype, width) uses the order that unpacks cheapest:
+//   kNatural : register (t, r) = codes (8t+2r, 8t+2r+1)
+//   kStride4 : register (t, r) = codes (8t+r, 8t+r+4)       (pairs 16 bits apart
+//              in a 4-bit word, 12 bits apart in a 24-bit int3 group)
+//   kStride8 : register (t, r) = codes (16(t/2)+4(t%2)+r, ... + 8)  (pairs 16
+//              bits apart in a 16-code int2 word)
+enum class Order { kNatural, kStride4, kStride8 };
+
 template <int DT, int BITS>
-__device__ inline u32x4 dequant8(uint32_t group, float zp, float scale)
+__host__ __device__ constexpr Order code_order()
 {
-    constexpr uint32_t mask = (1u << BITS) - 1u;
-    uint16_t h[8];
+    if (DT == kF16) return BITS == 2 ? Order::kStride8 : Order::kStride4;
+    return BITS == 3 ? Order::kStride4 : Order::kNatural;
+}
+
+__host__ __device__ constexpr int order_lo(Order o, int t, int r)
+{
+    return o == Order::kNatural   ? 8 * t + 2 * r
+           : o == Order::kStride4 ? 8 * t + r
+                                  : 16 * (t >> 1) + 4 * (t & 1) + r;
+}
+
+__host__ __device__ constexpr int order_hi(Order o, int t, int r)
+{
+    return o == Order::kNatural   ? 8 * t + 2 * r + 1
+           : o == Order::kStride4 ? 8 * t + r + 4
+                                  : 16 * (t >> 1) + 4 * (t & 1) + r + 8;
+}
+
+// Code number c (0..31) of a span.
+template <int BITS>
+__device__ inline uint32_t span_code(const Span<BITS>& s, int c)
+{
+    if constexpr (BITS == 4) return (s.w[c >> 3] >> (4 * (c & 7))) & 15u;
+    else if constexpr (BITS == 2) return (s.w[c >> 4] >> (2 * (c & 15))) & 3u;
+    else return (span_group<3>(s, c >> 3) >> (3 * (c & 7))) & 7u;
+}
+
+// 32 consecutive 16-bit A values (value 2i in the low half of in[i], 2i+1 in
+// the high half) -> the A registers of the four steps in order O:
+// out[4t+r] = (value order_lo(t,r), value order_hi(t,r)).
+template <Order O>
+__device__ inline void permute_span(const uint32_t (&in)[16], uint32_t (&out)[16])
+{
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float q = (float)((group >> (BITS * j)) & mask);
-        h[j] = Dt<DT>::from_float((q - zp) * scale);
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int lo = order_lo(O, t, r), hi = order_hi(O, t, r);
+            if constexpr (O == Order::kNatural) {
+                out[4 * t + r] = in[4 * t + r];
+            } else {
+                // v_perm_b32 picks bytes 0-3 from its second source, 4-7 from its first
+                const uint32_t sel = ((lo & 1) ? 0x0302u : 0x0100u) |
+                                     ((hi & 1) ? 0x07060000u : 0x05040000u);
+                out[4 * t + r] = __builtin_amdgcn_perm(in[hi >> 1], in[lo >> 1], sel);
+            }
+        }
     }
-    return u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+}
+
+// ---------------------------------------------------------------- dequant
+// Zero points that are multiples of 1/2 and below 256 in magnitude (integer
+// tensors, symmetric centres, the 1.5 offset of the int2 worked example) take
+// the fast routines below; others take dequant_step_generic.
+__host__ __device__ inline bool zp_is_half_integer(float zp)
+{
+    const float twice = zp * 2.0f;
+    return twice == (float)(int)twice && zp > -256.0f && zp < 256.0f;
+}
+
+// Step t of a span -> four registers of dtype pairs in code_order<DT,BITS>,
+// each value (code - zp) * scale rounded once to the dtype
+// [PR 33569: dequantized weights are rounded to the activation type before
+// accumulation].
+//
+// fp16: a code placed at mantissa bits 1.. of 0x6000 (512.0, spacing 0.5)
+// reads as 512 + code; subtracting 512 + zp is exact for half-integer zp, and
+// the packed multiply by the fp16 scale rounds once.
+// bf16: codes spread one per byte convert with v_cvt_f32_ubyte, one fma forms
+// code*s - zp*s = (code - zp)*s exactly in float32 (zp*s is exact for
+// half-integer zp and a 16-bit scale), v_cvt_pk_bf16_f32 rounds once.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// A loop-invariant value the compiler must keep in a register (VGPR or
+// SGPR) instead of folding it into a literal at every use.
+__device__ inline uint32_t opaque(uint32_t v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+__device__ inline uint32_t opaque_s(uint32_t v)
+{
+    asm("" : "+s"(v));  // not volatile: identical masks may be shared and hoisted
+    return v;
+}
+
+// (x & mask) | magic.  v_and_or_b32 has no literal-operand form on gfx950;
+// with the mask in an SGPR and the magic in a VGPR the compiler selects the
+// single instruction (and keeps track of its hazards itself).
+__device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic)
+{
+    return (x & opaque_s(mask)) | magic;
+}
+
+template <int DT, int BITS>
+__device__ inline u32x4 dequant_step(const Span<BITS>& sp, int t, float zp, float scale)
+{
+    u32x4 out;
+    if constexpr (DT == kF16) {
+        const uint32_t kMagic = opaque(0x60006000u);
+        const _Float16 c = (_Float16)(-(512.0f + zp));
+        const f16x2 c2 = {c, c};
+        const _Float16 sh = (_Float16)scale;
+        const f16x2 s2 = {sh, sh};
+        uint32_t raw[4];
+        if constexpr (BITS == 4) {
+            const uint32_t g = sp.w[t];
+            raw[0] = and_or(g << 1, 0x001e001eu, kMagic);
+#pragma unroll
+            for (int r = 1; r < 4; ++r) raw[r] = and_or(g >> (4 * r - 1), 0x001e001eu, kMagic);
+        } else if constexpr (BITS == 2) {
+            const uint32_t w = sp.w[t >> 1];
+            const int j0 = 4 * (t & 1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = j0 + r;
+                raw[r] = and_or(j == 0 ? (w << 1) : (w >> (2 * j - 1)), 0x00060006u, kMagic);
+            }
+        } else {
+            const uint32_t g = span_group<3>(sp, t);
+            const uint32_t y = (g & 0xfffu) | ((g << 4) & 0x0fff0000u);  // codes 4-7 to bit 16
+            raw[0] = and_or(y << 1, 0x000e000eu, kMagic);
+#pragma unroll
+            for (int r = 1; r < 4; ++r) raw[r] = and_or(y >> (3 * r - 1), 0x000e000eu, kMagic);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const f16x2 v = (__builtin_bit_cast(f16x2, raw[r]) + c2) * s2;
+            out[r] = __builtin_bit_cast(uint32_t, v);
+        }
+    } else {
+        const float c = -zp * scale;
+        auto cvt = [&](uint32_t x, int byte) {
+            return __builtin_fmaf((float)((x >> (8 * byte)) & 0xffu), scale, c);
+        };
+        auto pack_bf16 = [](float lo, float hi) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+            return __builtin_bit_cast(uint32_t, v);
+        };
+        if constexpr (BITS == 4) {
+            const uint32_t g = sp.w[t];
+            const uint32_t lo = g & 0x0f0f0f0fu, hi = (g >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[r] = pack_bf16(cvt(lo, r), cvt(hi, r));
+        } else if constexpr (BITS == 2) {
+            const uint32_t w = sp.w[t >> 1];
+            const int h = t & 1;
+            uint32_t b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b[i] = (w >> (2 * i)) & 0x03030303u;  // code c: byte c/4 of b[c%4]
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int byte = 2 * h + (r >> 1);
+                out[r] = pack_bf16(cvt(b[(r & 1) * 2], byte), cvt(b[(r & 1) * 2 + 1], byte));
+            }
+        } else {
+            const uint32_t g = span_group<3>(sp, t);
+            const uint32_t y = (g & 0xfffu) | ((g << 4) & 0x0fff0000u);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t z = (y >> (3 * r)) & 0x00070007u;  // codes r, r+4 in bytes 0, 2
+                out[r] = pack_bf16(cvt(z, 0), cvt(z, 2));
+            }
+        }
+    }
+    return out;
+}
+
+// ---------------------------------------------------------------- raw codes
+// For blocks spanning whole 128-input super-steps the decode kernel feeds the
+// MFMA the codes themselves, biased into exact dtype values: a code q placed
+// at mantissa bit 0 of 0x6400 (fp16 1024.0) or 0x4300 (bf16 128.0) reads as
+// kRawBias + q exactly.  The zero point and scale are applied afterwards in
+// float32: sum_k (q_k - zp) x_k = sum_k (kRawBias + q_k) x_k - (kRawBias + zp) sum_k x_k.
+// Both dtypes use the fp16 register orders here.
+template <int BITS>
+__host__ __device__ constexpr Order raw_order()
+{
+    return BITS == 2 ? Order::kStride8 : Order::kStride4;
+}
+
+template <int DT>
+__host__ __device__ constexpr float raw_bias()
+{
+    return DT == kF16 ? 1024.0f : 128.0f;
+}
+
+// dtype 1.0 in both halves (MFMA B operand of all ones: row sums of A)
+template <int DT>
+__host__ __device__ constexpr uint32_t ones2()
+{
+    return DT == kF16 ? 0x3c003c00u : 0x3f803f80u;
+}
+
+// (x & mask) | (y & ~mask): v_bfi_b32 with the mask in an SGPR
+__device__ inline uint32_t bfi(uint32_t mask, uint32_t x, uint32_t y)
+{
+    const uint32_t m = opaque_s(mask);
+    return (x & m) | (y & ~m);
+}
+
+template <int DT, int BITS>
+__device__ inline u32x4 raw_step(const Span<BITS>& sp, int t, uint32_t magic)
+{
+    u32x4 out;
+    if constexpr (BITS == 4) {
+        const uint32_t g = sp.w[t];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[r] = and_or(r == 0 ? g : g >> (4 * r), 0x000f000fu, magic);
+    } else if constexpr (BITS == 2) {
+        const uint32_t w = sp.w[t >> 1];
+        const int j0 = 4 * (t & 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = j0 + r;
+            out[r] = and_or(j == 0 ? w : w >> (2 * j), 0x00030003u, magic);
+        }
+    } else {
+        const uint32_t g = span_group<3>(sp, t);
+        const uint32_t y = bfi(0xfffu, g, g << 4);  // codes 4-7 to bit 16 (bits 12-15 unused)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[r] = and_or(r == 0 ? y : y >> (3 * r), 0x00070007u, magic);
+    }
+    return out;
+}
+
+// Any zero point: (code - zp) * scale in float32, rounded once to the dtype,
+// in the same register order as dequant_step.
+template <int DT, int BITS>
+__device__ inline u32x4 dequant_step_generic(const Span<BITS>& sp, int t, float zp, float scale)
+{
+    constexpr Order O = code_order<DT, BITS>();
+    u32x4 out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float lo = ((float)span_code<BITS>(sp, order_lo(O, t, r)) - zp) * scale;
+        const float hi = ((float)span_code<BITS>(sp, order_hi(O, t, r)) - zp) * scale;
+        out[r] = pack2(Dt<DT>::from_float(lo), Dt<DT>::from_float(hi));
+    }
+    return out;
 }
 
 // ---------------------------------------------------------------- activation

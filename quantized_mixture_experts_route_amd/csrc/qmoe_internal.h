@@ -9,20 +9,21 @@ namespace qmoe {
 
 // Tile shapes.  Prefill: a workgroup computes kPrefillMT routed rows of one
 // expert against 256 weight rows (4 waves x 4 MFMA column blocks of 16).
-// Decode: a workgroup computes up to 16 rows against 64 weight rows, its 4
-// waves splitting K.
+// Decode: a workgroup computes up to 16 rows against kDecodeFc{1,2}Blocks
+// column blocks of 16 weight rows, its 4 waves splitting K.
 constexpr int kPrefillMT = 128;
 constexpr int kPrefillWeightRows = 256;
 constexpr int kDecodeMT = 16;
-constexpr int kDecodeWeightRows = 64;
+constexpr int kDecodeFc1Blocks = 4;  // 64 weight rows = 32 gate/up pairs
+constexpr int kDecodeFc2Blocks = 2;  // 32 hidden columns
 constexpr int kSuperK = 128;  // inputs per K super-step: 4 lane groups x 32 codes
 
 // Output columns one work-list item covers (fc1 counts activation columns,
 // i.e. gate/up row pairs; fc2 counts hidden columns).
 constexpr int kPrefillFc1Cols = kPrefillWeightRows / 2;
 constexpr int kPrefillFc2Cols = kPrefillWeightRows;
-constexpr int kDecodeFc1Cols = kDecodeWeightRows / 2;
-constexpr int kDecodeFc2Cols = kDecodeWeightRows;
+constexpr int kDecodeFc1Cols = kDecodeFc1Blocks * 16 / 2;
+constexpr int kDecodeFc2Cols = kDecodeFc2Blocks * 16;
 
 struct ProjArgs {
     const uint8_t* codes;
@@ -30,6 +31,7 @@ struct ProjArgs {
     const uint8_t* zp;  // nullable
     float zp_fallback;  // fractional offset or symmetric centre
     int bits;
+    int fast;           // every zero point is a multiple of 1/2 below 256: fast dequant
 };
 
 // One grouped projection over a work-list.

@@ -112,6 +112,8 @@ def _projection_arrays(rng, E, N, K, bits, bs, dtype, mode):
         zp = synth._draw_zero_points(rng, E, N, K // bs, bits, 0, (1 << bits) - 1)
     elif mode == "zpo":
         zpo = 1.5 if bits == 2 else 2.5
+    elif mode == "zpo_generic":  # not a multiple of 1/2: the float32 dequant routine
+        zpo = 0.75 if bits == 2 else 3.25
     return codes, scales, zp, zpo
 
 
@@ -129,7 +131,7 @@ def _check_dequant(codes, scales, zp, zpo, bits, bs, dtype):
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("dtype", [1, 2])
-@pytest.mark.parametrize("mode", ["sym", "zpo", "u8"])
+@pytest.mark.parametrize("mode", ["sym", "zpo", "u8", "zpo_generic"])
 @pytest.mark.parametrize("bs", [16, 32, 128])
 def test_dequant_bit_exact(bits, dtype, mode, bs):
     rng = np.random.default_rng(bits * 100 + dtype * 10 + bs)
@@ -193,6 +195,29 @@ def test_layer_small(case):
     c = dict(SMALL[case])
     spec = synth.custom(name=f"small{case}", **c)
     _layer_check(spec, 500 + case)
+
+
+@pytest.mark.parametrize("bits", [(2, 2), (3, 4), (4, 3)])
+@pytest.mark.parametrize("dtype", [1, 2])
+@pytest.mark.parametrize("zp", ["sym", "zpo", "u8", "zpo_generic"])
+@pytest.mark.parametrize("bs", [128, 256])
+def test_layer_decode_blocks_of_whole_super_steps(bits, dtype, zp, bs):
+    # block_size a multiple of 128: the decode kernels apply zero point and
+    # scale per 128-input super-step on raw codes
+    zpo = {"sym": math.nan, "zpo": 1.5, "u8": math.nan, "zpo_generic": 0.75}[zp]
+    spec = synth.custom(T=5, H=512, I=256, E=4, k=2, fc1_bits=bits[0], fc2_bits=bits[1],
+                        block_size=bs, dtype=dtype, act=dtype - 1,
+                        zp_mode="u8" if zp == "u8" else ("zpo" if zp.startswith("zpo") else "sym"),
+                        zpo=zpo, zp_range=(0, 3), name=f"raw_{bits}_{dtype}_{zp}_{bs}")
+    _layer_check(spec, 7 + bs + dtype)
+
+
+@pytest.mark.parametrize("T,zpo", [(5, 0.75), (90, 0.75), (7, -1.25), (64, 2.25)])
+def test_layer_generic_zero_point_offset(T, zpo):
+    # offsets that are not multiples of 1/2 take the float32 dequant routine
+    spec = synth.custom(T=T, H=256, I=256, E=4, k=2, fc1_bits=2, fc2_bits=4, block_size=32,
+                        dtype=1 + T % 2, zp_mode="zpo", zpo=zpo, name=f"generic_zpo_{zpo}")
+    _layer_check(spec, 31 + T)
 
 
 @pytest.mark.parametrize("T,k", [(40, 2), (41, 2), (8, 10), (9, 10), (1, 1), (200, 4)])
