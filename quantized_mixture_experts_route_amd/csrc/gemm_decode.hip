@@ -3,22 +3,22 @@
 // When the expanded row count R = T*top_k is small [PR 33569: the decode
 // GEMV handles up to 80 expanded rows], each selected expert's weights are
 // streamed from HBM once per 16 of its rows, so time is set by packed-weight
-// bytes.  A workgroup takes one work-list item {expert, m, n}: up to 16 rows
-// of the expert against NB column blocks of 16 weight rows.  Its four
-// wavefronts split K (wavefront w takes super-steps w, w+4, ...); within a
-// wavefront the 16 rows ride in the rows of a 16x16x32 MFMA, so the row count
-// costs no VALU work and each weight element is dequantized once.
+// bytes and by how early those bytes are requested.  A workgroup of eight
+// wavefronts takes one decode work-list item {expert, n, row0, rows, ids[16]}
+// (one scalar fetch): up to 16 rows of the expert against NB column blocks of
+// 16 weight rows.  The wavefronts split K (wavefront w takes 128-input
+// super-steps w, w+8, ...); within a wavefront the 16 rows ride in the rows
+// of a 16x16x32 MFMA, so the row count costs no VALU work and each weight
+// element is dequantized once.
 //
-// Loads are ordered for latency.  The work-list item, the expert offsets and
-// the item's 16 sorted route ids are uniform across the workgroup and come
-// through scalar loads, which have their own counter, so they never hold up
-// the vector loads.  Right after the item is known a wavefront issues the
-// loads of a whole batch of super-steps (packed spans and the raw bits of
-// block scales and zero points, none of which is consumed yet), then the A
-// spans of its rows, and only then computes.  Each lane so keeps many loads
-// in flight against HBM latency.  The four partial
-// tiles are summed in LDS in a fixed order (no atomics), then the epilogue
-// applies the gated activation (fc1) or writes float32 rows (fc2).
+// Load order: the workgroup first requests its A rows (only the `rows` real
+// ones, coalesced 16-byte loads), then every wavefront issues the packed-code
+// spans and raw block scale / zero-point bits of all its super-steps, none of
+// which is consumed yet.  The A rows are written to LDS (permuted to the MFMA
+// register order) while the weight bytes are still in flight; each wavefront
+// then reads its A fragments from LDS.  The eight partial tiles are summed in
+// LDS in a fixed order (no atomics), then the epilogue applies the gated
+// activation (fc1) or writes float32 rows (fc2).
 //
 // RAW variant (block_size a multiple of 128, so every super-step lies in one
 // quantization block): the B operand is the raw codes biased into exact dtype
@@ -27,28 +27,27 @@
 // all-ones B operand, which yields the row sums of A:
 //   part = -(bias + zp) * rowsum + sum_t mfma(A_t, bias + codes_t)
 //   acc += scale * part
-// This halves the VALU work per weight, which is what bounds the kernel once
-// all loads are in flight.
 #include "gemm_common.h"
 
 namespace qmoe {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kBatch = 4;  // super-steps per wavefront whose loads are issued together
+constexpr int kBatch = 2;               // super-steps per wavefront per K chunk
+constexpr int kChunkK = kWaves * kBatch * kSuperK;  // 2048 inputs of A staged at a time
+constexpr int kPitch = kChunkK / 2 + 4;  // LDS row pitch in 32-bit words (+4 pad)
 
 template <int DT, int BITS, bool FC1, int NB, int ZP, bool RAW>
-__global__ __launch_bounds__(kThreads) void decode_kernel(ProjLaunch p,
-                                                          const int32_t* __restrict__ wl,
-                                                          const int32_t* __restrict__ offsets,
-                                                          const int32_t* __restrict__ sorted,
-                                                          const int32_t* __restrict__ n_items_ptr)
+__global__ __launch_bounds__(kThreads, 4) void decode_kernel(ProjLaunch p,
+                                                             const int32_t* __restrict__ items,
+                                                             const int32_t* __restrict__ n_items_ptr)
 {
     static_assert(!FC1 || NB % 2 == 0, "fc1 column blocks come in gate/up pairs");
+    static_assert(kWaves * kDecodeMT * (NB * 16 + 1) <= kDecodeMT * kPitch, "reduction fits");
     constexpr Order O = RAW ? raw_order<BITS>() : code_order<DT, BITS>();
     constexpr int kCols = NB * 16;  // weight rows per item
-    __shared__ float red[kWaves][kDecodeMT][kCols + 1];
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kDecodeMT * kPitch];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -56,7 +55,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(ProjLaunch p,
     const int g = lane >> 4;
     const int c = lane & 15;
     const int K = p.K;
-    const int n_super = K / kSuperK;
     const int n_items = *n_items_ptr;
     const bool two_blocks = p.block_size < 32;  // a 32-code span crosses a block boundary
     const uint16_t* a_src = reinterpret_cast<const uint16_t*>(p.a);
@@ -64,9 +62,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(ProjLaunch p,
     const u32x4 ones = {ones2<DT>(), ones2<DT>(), ones2<DT>(), ones2<DT>()};
 
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int e = wl[3 * item + 0];
-        const int mt = wl[3 * item + 1];
-        const int nt = wl[3 * item + 2];
+        const int32_t* it = items + (int64_t)kDecodeItemInts * item;
+        const int e = it[0];
+        const int nt = it[1];
+        const int row0 = it[2];
+        const int rows = it[3];
 
         int col0;
         WeightRow wr[NB];
@@ -90,16 +90,38 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(ProjLaunch p,
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        int row0 = 0, rows = 0, src = -1;
-        for (int s0 = wave; s0 < n_super; s0 += kWaves * kBatch) {
+        for (int kc = 0; kc < K; kc += kChunkK) {
+            const int kn = min(kChunkK, K - kc);
+            const int n_super = kn / kSuperK;
+            const int spans = kn / 32;  // 32-value A spans per row in this chunk
+
+            // 1) A rows of the chunk, first pass (up to 8 rows): one 64-byte span
+            //    per thread, requested before the weights
+            uint32_t a_stage[16];
+            const int a_spans = rows * spans;
+            auto load_a = [&](int q) {
+                const int64_t src = FC1 ? it[4 + q / spans] : row0 + q / spans;
+                load_a_span(a_src + src * K, kc + 32 * (q % spans), a_stage);
+            };
+            auto store_a = [&](int q) {
+                uint32_t perm[16];
+                permute_span<O>(a_stage, perm);
+                uint32_t* dst = lds + (q / spans) * kPitch + 16 * (q % spans);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    *reinterpret_cast<u32x4*>(dst + 4 * v) =
+                        u32x4{perm[4 * v], perm[4 * v + 1], perm[4 * v + 2], perm[4 * v + 3]};
+                }
+            };
+            if (tid < a_spans) load_a(tid);
+            // 2) packed weights of this wavefront's super-steps, not consumed yet
             Span<BITS> sp[kBatch][NB];
             RawParams rp[kBatch][NB];
-            uint32_t araw[kBatch][16];
 #pragma unroll
             for (int b = 0; b < kBatch; ++b) {
-                const int s = s0 + kWaves * b;
+                const int s = wave + kWaves * b;
                 if (s < n_super) {
-                    const int kk = s * kSuperK + 32 * g;
+                    const int kk = kc + s * kSuperK + 32 * g;
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
                         sp[b][nb] = load_span<BITS>(wr[nb].codes, kk);
@@ -107,88 +129,69 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(ProjLaunch p,
                     }
                 }
             }
-            if (s0 == wave) {
-                // rows of the item and the A row of this lane (routed row c); the
-                // 16 sorted ids are read as uniform scalars (the buffer has 16
-                // entries of slack) and lane c picks its own
-                row0 = offsets[e] + mt * kDecodeMT;
-                rows = min(kDecodeMT, offsets[e + 1] - row0);
-                int ids[kDecodeMT];
-#pragma unroll
-                for (int i = 0; i < kDecodeMT; ++i) ids[i] = sorted[row0 + i];
-                int mine = ids[0];
-#pragma unroll
-                for (int i = 1; i < kDecodeMT; ++i) mine = c == i ? ids[i] : mine;
-                src = c < rows ? (FC1 ? mine / p.top_k : row0 + c) : -1;
+            // 3) A rows to LDS in the MFMA register order (rows 8..15 in a second pass)
+            __syncthreads();  // previous chunk / item done with lds
+            if (tid < a_spans) store_a(tid);
+            if (tid + kThreads < a_spans) {
+                load_a(tid + kThreads);
+                store_a(tid + kThreads);
             }
-            const uint16_t* a_row = a_src + (int64_t)(src >= 0 ? src : 0) * K;
+            __syncthreads();
+
+            // 4) MFMAs; lanes of rows >= rows feed zeros
 #pragma unroll
             for (int b = 0; b < kBatch; ++b) {
-                const int s = s0 + kWaves * b;
-                if (s < n_super) {
-                    if (src >= 0) {
-                        load_a_span(a_row, s * kSuperK + 32 * g, araw[b]);
-                    } else {
+                const int s = wave + kWaves * b;
+                if (s >= n_super) continue;
+                const int kk = kc + s * kSuperK + 32 * g;
+                u32x4 a4[4];
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) araw[b][i] = 0u;
-                    }
+                for (int t = 0; t < 4; ++t) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(
+                        lds + c * kPitch + (s * kSuperK + 32 * g) / 2 + 4 * t);
+                    a4[t] = c < rows ? v : u32x4{0u, 0u, 0u, 0u};
                 }
-            }
+                if constexpr (RAW) {
+                    f32x4 rowsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const int s = s0 + kWaves * b;
-                if (s < n_super) {
-                    uint32_t af[16];
-                    permute_span<O>(araw[b], af);
-                    const int kk = s * kSuperK + 32 * g;
-                    if constexpr (RAW) {
-                        f32x4 rowsum = {0.f, 0.f, 0.f, 0.f};
+                    for (int t = 0; t < 4; ++t) rowsum = Dt<DT>::mfma(a4[t], ones, rowsum);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const BlockParams q = decode_params<DT, BITS, ZP>(rp[b][nb], p.w.zp_fallback);
+                        f32x4 part = rowsum * (-(raw_bias<DT>() + q.zp));
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
-                            const u32x4 a4 = {af[4 * t], af[4 * t + 1], af[4 * t + 2], af[4 * t + 3]};
-                            rowsum = Dt<DT>::mfma(a4, ones, rowsum);
+                            part = Dt<DT>::mfma(a4[t], raw_step<DT, BITS>(sp[b][nb], t, magic), part);
                         }
+                        acc[nb] += part * q.scale;
+                    }
+                } else {
 #pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) {
-                            const BlockParams q = decode_params<DT, BITS, ZP>(rp[b][nb], p.w.zp_fallback);
-                            f32x4 part = rowsum * (-(raw_bias<DT>() + q.zp));
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const BlockParams q0 = decode_params<DT, BITS, ZP>(rp[b][nb], p.w.zp_fallback);
 #pragma unroll
-                            for (int t = 0; t < 4; ++t) {
-                                const u32x4 a4 = {af[4 * t], af[4 * t + 1], af[4 * t + 2], af[4 * t + 3]};
-                                part = Dt<DT>::mfma(a4, raw_step<DT, BITS>(sp[b][nb], t, magic), part);
+                        for (int t = 0; t < 4; ++t) {
+                            BlockParams q = q0;
+                            if (two_blocks && t >= 2) {
+                                q = decode_params<DT, BITS, ZP>(
+                                    load_params<ZP>(wr[nb], kk + 16, p.block_size), p.w.zp_fallback);
                             }
-                            acc[nb] += part * q.scale;
-                        }
-                    } else {
-#pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) {
-                            const BlockParams q0 = decode_params<DT, BITS, ZP>(rp[b][nb], p.w.zp_fallback);
-#pragma unroll
-                            for (int t = 0; t < 4; ++t) {
-                                BlockParams q = q0;
-                                if (two_blocks && t >= 2) {
-                                    q = decode_params<DT, BITS, ZP>(
-                                        load_params<ZP>(wr[nb], kk + 16, p.block_size), p.w.zp_fallback);
-                                }
-                                const u32x4 a4 = {af[4 * t], af[4 * t + 1], af[4 * t + 2], af[4 * t + 3]};
-                                const u32x4 bf = dequant_zp<DT, BITS, ZP>(sp[b][nb], t, q);
-                                acc[nb] = Dt<DT>::mfma(a4, bf, acc[nb]);
-                            }
+                            const u32x4 bf = dequant_zp<DT, BITS, ZP>(sp[b][nb], t, q);
+                            acc[nb] = Dt<DT>::mfma(a4[t], bf, acc[nb]);
                         }
                     }
                 }
             }
         }
 
-        if (n_super <= wave) {  // this wavefront had no super-step: still needs the rows
-            row0 = offsets[e] + mt * kDecodeMT;
-            rows = min(kDecodeMT, offsets[e + 1] - row0);
-        }
-        __syncthreads();  // the previous item is done reading red
+        // 5) sum the eight partial tiles in LDS (fixed order), then the epilogue
+        __syncthreads();  // every wavefront is done reading A from lds
+        float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) red[wave][4 * g + i][nb * 16 + c] = acc[nb][i];
+            for (int i = 0; i < 4; ++i)
+                red[(wave * kDecodeMT + 4 * g + i) * (kCols + 1) + nb * 16 + c] = acc[nb][i];
         __syncthreads();
 
         if constexpr (FC1) {
@@ -202,8 +205,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(ProjLaunch p,
                 float gate = 0.f, up = 0.f;
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w) {
-                    gate += red[w][m][gate_col];
-                    up += red[w][m][gate_col + 16];
+                    gate += red[(w * kDecodeMT + m) * (kCols + 1) + gate_col];
+                    up += red[(w * kDecodeMT + m) * (kCols + 1) + gate_col + 16];
                 }
                 uint16_t* out = reinterpret_cast<uint16_t*>(p.act_out) + (int64_t)(row0 + m) * I;
                 out[col0 + j] = Dt<DT>::from_float(act_value<DT>(p.act, gate, up));
@@ -215,10 +218,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(ProjLaunch p,
                 if (m >= rows) continue;
                 float v = 0.f;
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) v += red[w][m][h];
-                p.y2[(int64_t)sorted[row0 + m] * p.N + col0 + h] = v;
+                for (int w = 0; w < kWaves; ++w) v += red[(w * kDecodeMT + m) * (kCols + 1) + h];
+                p.y2[(int64_t)it[4 + m] * p.N + col0 + h] = v;  // route id of row m
             }
         }
+        __syncthreads();  // the next item reuses lds
     }
 }
 
@@ -226,7 +230,7 @@ template <bool FC1, int DT, int NB, int BITS, int ZP, bool RAW>
 hipError_t launch_one(const ProjLaunch& p, hipStream_t s)
 {
     hipLaunchKernelGGL((decode_kernel<DT, BITS, FC1, NB, ZP, RAW>), dim3((unsigned)p.grid),
-                       dim3(kThreads), 0, s, p, p.worklist, p.offsets, p.sorted, p.n_items);
+                       dim3(kThreads), 0, s, p, p.worklist, p.n_items);
     return hipGetLastError();
 }
 

@@ -119,10 +119,11 @@ bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L)
     L->ids = take((size_t)R * 4);
     L->w = take((size_t)R * 4);
     L->offsets = take(((size_t)E + 1) * 4);
-    L->sorted = take(((size_t)R + qmoe::kDecodeMT) * 4);  // slack: decode reads 16 ids per item
-    L->wl1 = take((size_t)(L->cap1 > 0 ? L->cap1 : 1) * 12);
+    L->sorted = take((size_t)R * 4);
+    const size_t item_bytes = L->decode ? qmoe::kDecodeItemInts * 4 : 12;
+    L->wl1 = take((size_t)(L->cap1 > 0 ? L->cap1 : 1) * item_bytes);
     L->n1 = take(4);
-    L->wl2 = take((size_t)(L->cap2 > 0 ? L->cap2 : 1) * 12);
+    L->wl2 = take((size_t)(L->cap2 > 0 ? L->cap2 : 1) * item_bytes);
     L->n2 = take(4);
     L->act = take((size_t)act_bytes);
     L->y2 = take((size_t)y2_bytes);
@@ -242,7 +243,7 @@ int qmoe_group(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int
     timer_begin(QMOE_STAGE_GROUP, s);
     const hipError_t e = qmoe::launch_group(topk_ids, (int)R, E, m_tile, (int)ceil_div(N, n_tile),
                                             expert_offsets, sorted_routes, worklist,
-                                            worklist_capacity, n_items, 0, nullptr, 0, nullptr, s);
+                                            worklist_capacity, n_items, 0, nullptr, 0, nullptr, 0, s);
     timer_end(QMOE_STAGE_GROUP, s);
     return e == hipSuccess ? ok() : hip_fail(e, "group launch");
 }
@@ -323,7 +324,7 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
 
     timer_begin(QMOE_STAGE_GROUP, s);
     e = qmoe::launch_group(ids, (int)R, E, L.m_tile, L.nt1, offsets, sorted, wl1, L.cap1, n1, L.nt2,
-                           wl2, L.cap2, n2, s);
+                           wl2, L.cap2, n2, L.decode ? top_k : 0, s);
     timer_end(QMOE_STAGE_GROUP, s);
     if (e != hipSuccess) return hip_fail(e, "group launch");
 

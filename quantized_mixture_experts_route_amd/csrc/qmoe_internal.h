@@ -25,6 +25,12 @@ constexpr int kPrefillFc2Cols = kPrefillWeightRows;
 constexpr int kDecodeFc1Cols = kDecodeFc1Blocks * 16 / 2;
 constexpr int kDecodeFc2Cols = kDecodeFc2Blocks * 16;
 
+// Decode work-list items carry everything a workgroup needs in one scalar
+// fetch: {expert, n_tile, first sorted row, rows, ids[16]} where ids are the
+// rows' token ids (fc1 list) or route ids (fc2 list), 0 past `rows`.
+constexpr int kDecodeItemInts = 20;
+constexpr int kDecodeMaxRoutes = 128;  // LDS copy of the sorted routes in the group kernel
+
 struct ProjArgs {
     const uint8_t* codes;
     const void* scales;
@@ -55,9 +61,11 @@ struct ProjLaunch {
 hipError_t launch_route(const float* logits, int64_t T, int E, int top_k, int normalize,
                         int32_t* ids, float* weights, hipStream_t s);
 
+// rich_top_k > 0: decode lists of kDecodeItemInts-int items (m_tile must be
+// kDecodeMT and R <= kDecodeMaxRoutes); 0: {expert, m, n} triples.
 hipError_t launch_group(const int32_t* ids, int R, int E, int m_tile, int nt1, int32_t* offsets,
                         int32_t* sorted, int32_t* wl1, int64_t cap1, int32_t* n1, int nt2,
-                        int32_t* wl2, int64_t cap2, int32_t* n2, hipStream_t s);
+                        int32_t* wl2, int64_t cap2, int32_t* n2, int rich_top_k, hipStream_t s);
 
 hipError_t launch_fc1_prefill(const ProjLaunch& p, int dtype, hipStream_t s);
 hipError_t launch_fc2_prefill(const ProjLaunch& p, int dtype, hipStream_t s);
