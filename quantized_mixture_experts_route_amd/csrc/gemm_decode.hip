@@ -4,21 +4,24 @@
 // GEMV handles up to 80 expanded rows], each selected expert's weights are
 // streamed from HBM once per 16 of its rows, so time is set by packed-weight
 // bytes and by how early those bytes are requested.  A workgroup of eight
-// wavefronts takes one decode work-list item {expert, n, row0, rows, ids[16]}
-// (one scalar fetch): up to 16 rows of the expert against NB column blocks of
-// 16 weight rows.  The wavefronts split K (wavefront w takes 128-input
+// wavefronts takes one item (m-tile i / nt, column block i % nt): up to 16
+// rows of one expert, described by the m-tile {expert, row0, rows, 0,
+// token ids[16], route ids[16]} (one scalar fetch), against NB column blocks
+// of 16 weight rows.  The wavefronts split K (wavefront w takes 128-input
 // super-steps w, w+8, ...); within a wavefront the 16 rows ride in the rows
 // of a 16x16x32 MFMA, so the row count costs no VALU work and each weight
 // element is dequantized once.
 //
-// Load order: the workgroup first requests its A rows (only the `rows` real
-// ones, coalesced 16-byte loads), then every wavefront issues the packed-code
-// spans and raw block scale / zero-point bits of all its super-steps, none of
-// which is consumed yet.  The A rows are written to LDS (permuted to the MFMA
-// register order) while the weight bytes are still in flight; each wavefront
-// then reads its A fragments from LDS.  The eight partial tiles are summed in
-// LDS in a fixed order (no atomics), then the epilogue applies the gated
-// activation (fc1) or writes float32 rows (fc2).
+// Load order: the wavefront requests its A row (tile row `wave`; the row ids
+// come with the m-tile as scalar loads), then the item's scales for the K
+// chunk (one 16-byte unit per thread, STAGED), then the packed-code spans of
+// all its super-steps, none of which is consumed yet.  Every load is issued
+// unconditionally (indices are clamped) so that each wait covers exactly the
+// loads it needs.  The A rows (permuted to the MFMA register order) and the
+// scale table are written to LDS while the weight bytes are still in flight;
+// each wavefront then reads its A fragments and scales from LDS.  The eight
+// partial tiles are summed in LDS in a fixed order (no atomics), then the
+// epilogue applies the gated activation (fc1) or writes float32 rows (fc2).
 //
 // RAW variant (block_size a multiple of 128, so every super-step lies in one
 // quantization block): the B operand is the raw codes biased into exact dtype
@@ -37,53 +40,64 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kBatch = 2;               // super-steps per wavefront per K chunk
 constexpr int kChunkK = kWaves * kBatch * kSuperK;  // 2048 inputs of A staged at a time
 constexpr int kPitch = kChunkK / 2 + 4;  // LDS row pitch in 32-bit words (+4 pad)
+constexpr int kScPitch = kChunkK / 32 + 4;  // staged scale row pitch in uint16 (+4 pad)
 
-template <int DT, int BITS, bool FC1, int NB, int ZP, bool RAW>
+// Staged scales (STAGED): the scales of the item's weight rows for the K
+// chunk are one 16-byte load per thread into an LDS table instead of one
+// 2-byte load per lane, column block and super-step.  Needs a constant zero
+// point, 32 <= block_size <= 256, a multiple of 8 blocks per row and
+// 16-byte aligned scales (checked by the launcher).
+template <int DT, int BITS, bool FC1, int NB, int ZP, bool RAW, bool STAGED>
 __global__ __launch_bounds__(kThreads, 4) void decode_kernel(ProjLaunch p,
-                                                             const int32_t* __restrict__ items,
-                                                             const int32_t* __restrict__ n_items_ptr)
+                                                             const int32_t* __restrict__ tiles,
+                                                             const int32_t* __restrict__ n_tiles_ptr)
 {
     static_assert(!FC1 || NB % 2 == 0, "fc1 column blocks come in gate/up pairs");
     static_assert(kWaves * kDecodeMT * (NB * 16 + 1) <= kDecodeMT * kPitch, "reduction fits");
+    static_assert(!STAGED || ZP == kZpConst, "the staged table holds scales only");
     constexpr Order O = RAW ? raw_order<BITS>() : code_order<DT, BITS>();
     constexpr int kCols = NB * 16;  // weight rows per item
+    static_assert(kCols * (kChunkK / 32) / 8 <= kThreads, "one staged unit per thread");
     __shared__ __attribute__((aligned(16))) uint32_t lds[kDecodeMT * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t sc_tab[STAGED ? kCols * kScPitch : 8];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int g = lane >> 4;
     const int c = lane & 15;
     const int K = p.K;
-    const int n_items = *n_items_ptr;
-    const bool two_blocks = p.block_size < 32;  // a 32-code span crosses a block boundary
+    const int bs = p.block_size;
+    const int n_blocks = K / bs;
+    const int nt = p.N / kCols;  // column blocks of one m-tile
+    const int n_items = *n_tiles_ptr * nt;
+    const bool two_blocks = bs < 32;  // a 32-code span crosses a block boundary
     const uint16_t* a_src = reinterpret_cast<const uint16_t*>(p.a);
+    const uint16_t* scales = reinterpret_cast<const uint16_t*>(p.w.scales);
     const uint32_t magic = opaque(DT == kF16 ? 0x64006400u : 0x43004300u);
     const u32x4 ones = {ones2<DT>(), ones2<DT>(), ones2<DT>(), ones2<DT>()};
 
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int32_t* it = items + (int64_t)kDecodeItemInts * item;
+        const int tile = item / nt;
+        const int n = item - tile * nt;
+        const int32_t* it = tiles + (int64_t)kDecodeTileInts * tile;
         const int e = it[0];
-        const int nt = it[1];
-        const int row0 = it[2];
-        const int rows = it[3];
+        const int row0 = it[1];
+        const int rows = it[2];
+        // A rows this wavefront stages: tile rows `wave` and `wave + 8`
+        const int64_t a_row1 = FC1 ? it[kDecodeTileTokens + wave] : row0 + wave;
+        const int64_t a_row2 = FC1 ? it[kDecodeTileTokens + wave + kWaves] : row0 + wave + kWaves;
 
-        int col0;
+        // weight rows of the item: fc1 rows 2*col0 .. 2*col0+63 (gate/up
+        // interleaved), fc2 rows col0 .. col0+31; table row of (nb, c)
+        const int col0 = FC1 ? n * (kCols / 2) : n * kCols;
+        const int64_t wrow0 = (int64_t)e * p.N + (FC1 ? 2 * col0 : col0);
+        int trow[NB];
         WeightRow wr[NB];
-        if constexpr (FC1) {
-            col0 = nt * (kCols / 2);  // first activation column
 #pragma unroll
-            for (int q = 0; q < NB / 2; ++q) {
-                const int64_t gate = (int64_t)e * p.N + 2 * (col0 + 16 * q + c);
-                wr[2 * q] = weight_row(p.w, gate, K, p.block_size);
-                wr[2 * q + 1] = weight_row(p.w, gate + 1, K, p.block_size);
-            }
-        } else {
-            col0 = nt * kCols;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                wr[nb] = weight_row(p.w, (int64_t)e * p.N + col0 + 16 * nb + c, K, p.block_size);
-            }
+        for (int nb = 0; nb < NB; ++nb) {
+            trow[nb] = FC1 ? 32 * (nb / 2) + 2 * c + (nb & 1) : 16 * nb + c;
+            wr[nb] = weight_row(p.w, wrow0 + trow[nb], K, bs);
         }
 
         f32x4 acc[NB];
@@ -93,52 +107,66 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(ProjLaunch p,
         for (int kc = 0; kc < K; kc += kChunkK) {
             const int kn = min(kChunkK, K - kc);
             const int n_super = kn / kSuperK;
-            const int spans = kn / 32;  // 32-value A spans per row in this chunk
+            const int spans = kn / 32;            // 32-value A spans per row in this chunk
+            const int sl = min(lane, spans - 1);  // this lane's span (clamped: loads stay in bounds)
 
-            // 1) A rows of the chunk, first pass (up to 8 rows): one 64-byte span
-            //    per thread, requested before the weights
+            // 1) A rows 0..7 of the tile, one row per wavefront, one 64-byte span
+            //    per lane, requested before the weights (row ids are scalar loads)
             uint32_t a_stage[16];
-            const int a_spans = rows * spans;
-            auto load_a = [&](int q) {
-                const int64_t src = FC1 ? it[4 + q / spans] : row0 + q / spans;
-                load_a_span(a_src + src * K, kc + 32 * (q % spans), a_stage);
-            };
-            auto store_a = [&](int q) {
+            if (wave < rows) load_a_span(a_src + a_row1 * K, kc + 32 * sl, a_stage);
+            // 2) staged scales: one 16-byte unit of the chunk's table per thread
+            u32x4 sc_unit = {0u, 0u, 0u, 0u};
+            int sc_row = 0, sc_part = 0, n_units = 0;
+            if constexpr (STAGED) {
+                const int upr = kn / bs / 8;  // units per row
+                n_units = kCols * upr;
+                const int u = min(tid, n_units - 1);
+                sc_row = u / upr;
+                sc_part = u - sc_row * upr;
+                sc_unit = *reinterpret_cast<const u32x4*>(
+                    scales + (wrow0 + sc_row) * n_blocks + kc / bs + 8 * sc_part);
+            }
+            // 3) packed weights of this wavefront's super-steps, not consumed yet
+            //    (super-steps past the chunk reload the last one and are skipped)
+            Span<BITS> sp[kBatch][NB];
+            RawParams rp[kBatch][NB];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int s = min(wave + kWaves * b, n_super - 1);
+                const int kk = kc + s * kSuperK + 32 * g;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    sp[b][nb] = load_span<BITS>(wr[nb].codes, kk);
+                    if constexpr (!STAGED) rp[b][nb] = load_params<ZP>(wr[nb], kk, bs);
+                }
+            }
+            // 4) A rows and scales to LDS; A in the MFMA register order
+            auto store_a = [&](int row) {
                 uint32_t perm[16];
                 permute_span<O>(a_stage, perm);
-                uint32_t* dst = lds + (q / spans) * kPitch + 16 * (q % spans);
+                uint32_t* dst = lds + row * kPitch + 16 * lane;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     *reinterpret_cast<u32x4*>(dst + 4 * v) =
                         u32x4{perm[4 * v], perm[4 * v + 1], perm[4 * v + 2], perm[4 * v + 3]};
                 }
             };
-            if (tid < a_spans) load_a(tid);
-            // 2) packed weights of this wavefront's super-steps, not consumed yet
-            Span<BITS> sp[kBatch][NB];
-            RawParams rp[kBatch][NB];
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const int s = wave + kWaves * b;
-                if (s < n_super) {
-                    const int kk = kc + s * kSuperK + 32 * g;
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        sp[b][nb] = load_span<BITS>(wr[nb].codes, kk);
-                        rp[b][nb] = load_params<ZP>(wr[nb], kk, p.block_size);
-                    }
+            __syncthreads();  // previous chunk / item done with lds and sc_tab
+            if (wave < rows && lane < spans) store_a(wave);
+            if constexpr (STAGED) {
+                if (tid < n_units) {
+                    uint32_t* dst = reinterpret_cast<uint32_t*>(sc_tab + sc_row * kScPitch + 8 * sc_part);
+                    *reinterpret_cast<u32x2*>(dst) = u32x2{sc_unit.x, sc_unit.y};
+                    *reinterpret_cast<u32x2*>(dst + 2) = u32x2{sc_unit.z, sc_unit.w};
                 }
             }
-            // 3) A rows to LDS in the MFMA register order (rows 8..15 in a second pass)
-            __syncthreads();  // previous chunk / item done with lds
-            if (tid < a_spans) store_a(tid);
-            if (tid + kThreads < a_spans) {
-                load_a(tid + kThreads);
-                store_a(tid + kThreads);
+            if (wave + kWaves < rows) {  // rows 8..15 (rare): after the weights
+                load_a_span(a_src + a_row2 * K, kc + 32 * sl, a_stage);
+                if (lane < spans) store_a(wave + kWaves);
             }
             __syncthreads();
 
-            // 4) MFMAs; lanes of rows >= rows feed zeros
+            // 5) MFMAs; lanes of rows >= rows feed zeros
 #pragma unroll
             for (int b = 0; b < kBatch; ++b) {
                 const int s = wave + kWaves * b;
@@ -151,13 +179,23 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(ProjLaunch p,
                         lds + c * kPitch + (s * kSuperK + 32 * g) / 2 + 4 * t);
                     a4[t] = c < rows ? v : u32x4{0u, 0u, 0u, 0u};
                 }
+                auto params = [&](int nb, int kin) {
+                    if constexpr (STAGED) {
+                        BlockParams q;
+                        q.zp = p.w.zp_fallback;
+                        q.scale = Dt<DT>::to_float(sc_tab[trow[nb] * kScPitch + (kin - kc) / bs]);
+                        return q;
+                    } else {
+                        return decode_params<DT, BITS, ZP>(rp[b][nb], p.w.zp_fallback);
+                    }
+                };
                 if constexpr (RAW) {
                     f32x4 rowsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int t = 0; t < 4; ++t) rowsum = Dt<DT>::mfma(a4[t], ones, rowsum);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
-                        const BlockParams q = decode_params<DT, BITS, ZP>(rp[b][nb], p.w.zp_fallback);
+                        const BlockParams q = params(nb, kc + s * kSuperK);
                         f32x4 part = rowsum * (-(raw_bias<DT>() + q.zp));
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
@@ -168,13 +206,13 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(ProjLaunch p,
                 } else {
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
-                        const BlockParams q0 = decode_params<DT, BITS, ZP>(rp[b][nb], p.w.zp_fallback);
+                        const BlockParams q0 = params(nb, kk);
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
                             BlockParams q = q0;
-                            if (two_blocks && t >= 2) {
+                            if (!STAGED && two_blocks && t >= 2) {
                                 q = decode_params<DT, BITS, ZP>(
-                                    load_params<ZP>(wr[nb], kk + 16, p.block_size), p.w.zp_fallback);
+                                    load_params<ZP>(wr[nb], kk + 16, bs), p.w.zp_fallback);
                             }
                             const u32x4 bf = dequant_zp<DT, BITS, ZP>(sp[b][nb], t, q);
                             acc[nb] = Dt<DT>::mfma(a4[t], bf, acc[nb]);
@@ -182,9 +220,12 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(ProjLaunch p,
                     }
                 }
             }
+            // Loads of skipped super-steps are still in flight here; draining them
+            // now keeps the next chunk's loads from waiting on stale registers.
+            __builtin_amdgcn_s_waitcnt(0);
         }
 
-        // 5) sum the eight partial tiles in LDS (fixed order), then the epilogue
+        // 6) sum the eight partial tiles in LDS (fixed order), then the epilogue
         __syncthreads();  // every wavefront is done reading A from lds
         float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
@@ -219,34 +260,44 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(ProjLaunch p,
                 float v = 0.f;
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w) v += red[(w * kDecodeMT + m) * (kCols + 1) + h];
-                p.y2[(int64_t)it[4 + m] * p.N + col0 + h] = v;  // route id of row m
+                p.y2[(int64_t)it[kDecodeTileRoutes + m] * p.N + col0 + h] = v;
             }
         }
         __syncthreads();  // the next item reuses lds
     }
 }
 
-template <bool FC1, int DT, int NB, int BITS, int ZP, bool RAW>
+template <bool FC1, int DT, int NB, int BITS, int ZP, bool RAW, bool STAGED = false>
 hipError_t launch_one(const ProjLaunch& p, hipStream_t s)
 {
-    hipLaunchKernelGGL((decode_kernel<DT, BITS, FC1, NB, ZP, RAW>), dim3((unsigned)p.grid),
+    hipLaunchKernelGGL((decode_kernel<DT, BITS, FC1, NB, ZP, RAW, STAGED>), dim3((unsigned)p.grid),
                        dim3(kThreads), 0, s, p, p.worklist, p.n_items);
     return hipGetLastError();
+}
+
+// Scales can be staged when every K chunk covers whole 16-byte units of every
+// weight row's scales.
+inline bool can_stage(const ProjLaunch& p)
+{
+    const int bs = p.block_size;
+    return bs >= 32 && bs <= 256 && (p.K / bs) % 8 == 0 &&
+           reinterpret_cast<uintptr_t>(p.w.scales) % 16 == 0;
 }
 
 template <bool FC1, int DT, int NB, int BITS>
 hipError_t launch_zp(const ProjLaunch& p, hipStream_t s)
 {
     const int zp = zp_mode(p.w);
+    const bool staged = zp != kZpTensor && can_stage(p);
     if (p.block_size % kSuperK == 0) {  // zero point applied in float32: any value works
-        return zp == kZpTensor ? launch_one<FC1, DT, NB, BITS, kZpTensor, true>(p, s)
-                               : launch_one<FC1, DT, NB, BITS, kZpConst, true>(p, s);
+        if (zp == kZpTensor) return launch_one<FC1, DT, NB, BITS, kZpTensor, true>(p, s);
+        return staged ? launch_one<FC1, DT, NB, BITS, kZpConst, true, true>(p, s)
+                      : launch_one<FC1, DT, NB, BITS, kZpConst, true>(p, s);
     }
-    switch (zp) {
-    case kZpConst: return launch_one<FC1, DT, NB, BITS, kZpConst, false>(p, s);
-    case kZpTensor: return launch_one<FC1, DT, NB, BITS, kZpTensor, false>(p, s);
-    default: return launch_one<FC1, DT, NB, BITS, kZpGeneric, false>(p, s);
-    }
+    if (zp == kZpTensor) return launch_one<FC1, DT, NB, BITS, kZpTensor, false>(p, s);
+    if (zp == kZpConst && staged) return launch_one<FC1, DT, NB, BITS, kZpConst, false, true>(p, s);
+    // any other constant zero point: float32 dequant (exact for the fast values too)
+    return launch_one<FC1, DT, NB, BITS, kZpGeneric, false>(p, s);
 }
 
 template <bool FC1, int DT, int NB>

@@ -57,12 +57,9 @@ __device__ int block_exclusive_scan(int* v, int n, int* part)
     return total;
 }
 
-// Emits work-list items for items [0, min(total, cap)): {e, m, n} triples,
-// or with rich_top_k > 0 decode items {e, n, row0, rows, ids[16]} whose ids
-// are token ids (list 1, route / top_k) or route ids (list 2).
+// Emits work-list triples {e, m, n} for items [0, min(total, cap)).
 __device__ void emit_items(const int* item_base, int E, int n_tiles, int total, int32_t* wl,
-                           int64_t cap, int rich_top_k, bool token_ids, const int* offs,
-                           const int* s_sorted, int m_tile)
+                           int64_t cap)
 {
     const int64_t limit = total < cap ? total : cap;
     for (int64_t idx = threadIdx.x; idx < limit; idx += kThreads) {
@@ -74,31 +71,9 @@ __device__ void emit_items(const int* item_base, int E, int n_tiles, int total, 
             if (item_base[mid] <= idx) lo = mid; else hi = mid - 1;
         }
         const int local = (int)idx - item_base[lo];
-        const int m = local / n_tiles;
-        const int n = local % n_tiles;
-        if (rich_top_k <= 0) {
-            wl[3 * idx + 0] = lo;
-            wl[3 * idx + 1] = m;
-            wl[3 * idx + 2] = n;
-            continue;
-        }
-        const int row0 = offs[lo] + m * m_tile;
-        const int rows = min(m_tile, offs[lo + 1] - row0);
-        int v[kDecodeItemInts];
-        v[0] = lo;
-        v[1] = n;
-        v[2] = row0;
-        v[3] = rows;
-#pragma unroll
-        for (int i = 0; i < kDecodeMT; ++i) {
-            const int route = i < rows ? s_sorted[row0 + i] : 0;
-            v[4 + i] = token_ids ? route / rich_top_k : route;
-        }
-        int4* dst = reinterpret_cast<int4*>(wl + (int64_t)kDecodeItemInts * idx);
-#pragma unroll
-        for (int q = 0; q < kDecodeItemInts / 4; ++q) {
-            dst[q] = make_int4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-        }
+        wl[3 * idx + 0] = lo;
+        wl[3 * idx + 1] = local / n_tiles;
+        wl[3 * idx + 2] = local % n_tiles;
     }
 }
 
@@ -106,14 +81,12 @@ __global__ __launch_bounds__(kThreads) void group_kernel(
     const int32_t* __restrict__ ids, int R, int E, int m_tile, int nt1,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ wl1,
     int64_t cap1, int32_t* __restrict__ n1, int nt2, int32_t* __restrict__ wl2, int64_t cap2,
-    int32_t* __restrict__ n2, int rich_top_k)
+    int32_t* __restrict__ n2)
 {
     __shared__ int cnt[kWaves][kMaxExperts];
     __shared__ int total[kMaxExperts];
     __shared__ int items[kMaxExperts];
     __shared__ int part[kThreads];
-    __shared__ int offs[kMaxExperts + 1];           // expert offsets (rich items)
-    __shared__ int s_sorted[kDecodeMaxRoutes];      // sorted routes (rich items)
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -149,13 +122,9 @@ __global__ __launch_bounds__(kThreads) void group_kernel(
     const int grouped = block_exclusive_scan(total, E, part);  // total[e] -> offsets[e]
     for (int e = tid; e < E; e += kThreads) {
         offsets[e] = total[e];
-        offs[e] = total[e];
         for (int w = 0; w < kWaves; ++w) cnt[w][e] += total[e];
     }
-    if (tid == 0) {
-        offsets[E] = grouped;
-        offs[E] = grouped;
-    }
+    if (tid == 0) offsets[E] = grouped;
     __syncthreads();
 
     // pass 2: stable placement, one wavefront per segment, 64 routes at a time
@@ -175,7 +144,6 @@ __global__ __launch_bounds__(kThreads) void group_kernel(
             const int rank = __popcll(below);
             const int pos = cnt[wave][e] + rank;
             sorted[pos] = r;
-            if (rich_top_k > 0) s_sorted[pos] = r;
         }
         __builtin_amdgcn_wave_barrier();
         if (valid && (peers >> lane) == 1ull) {  // highest lane of its peer set
@@ -195,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void group_kernel(
         for (int e = tid; e < E; e += kThreads) total[e] = items[e] * nt;
         __syncthreads();
         const int n_total = block_exclusive_scan(total, E, part);
-        emit_items(total, E, nt, n_total, wl, cap, rich_top_k, pass == 0, offs, s_sorted, m_tile);
+        emit_items(total, E, nt, n_total, wl, cap);
         if (tid == 0) *n_out = n_total;
         __syncthreads();
     }
@@ -205,11 +173,10 @@ __global__ __launch_bounds__(kThreads) void group_kernel(
 
 hipError_t launch_group(const int32_t* ids, int R, int E, int m_tile, int nt1, int32_t* offsets,
                         int32_t* sorted, int32_t* wl1, int64_t cap1, int32_t* n1, int nt2,
-                        int32_t* wl2, int64_t cap2, int32_t* n2, int rich_top_k, hipStream_t s)
+                        int32_t* wl2, int64_t cap2, int32_t* n2, hipStream_t s)
 {
-    if (rich_top_k > 0 && (m_tile != kDecodeMT || R > kDecodeMaxRoutes)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), 0, s, ids, R, E, m_tile, nt1,
-                       offsets, sorted, wl1, cap1, n1, nt2, wl2, cap2, n2, rich_top_k);
+                       offsets, sorted, wl1, cap1, n1, nt2, wl2, cap2, n2);
     return hipGetLastError();
 }
 

@@ -120,11 +120,17 @@ bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L)
     L->w = take((size_t)R * 4);
     L->offsets = take(((size_t)E + 1) * 4);
     L->sorted = take((size_t)R * 4);
-    const size_t item_bytes = L->decode ? qmoe::kDecodeItemInts * 4 : 12;
-    L->wl1 = take((size_t)(L->cap1 > 0 ? L->cap1 : 1) * item_bytes);
-    L->n1 = take(4);
-    L->wl2 = take((size_t)(L->cap2 > 0 ? L->cap2 : 1) * item_bytes);
-    L->n2 = take(4);
+    if (L->decode) {  // one m-tile list serves both projections
+        L->wl1 = take((size_t)m_tiles * qmoe::kDecodeTileInts * 4);
+        L->n1 = take(4);
+        L->wl2 = L->wl1;
+        L->n2 = L->n1;
+    } else {
+        L->wl1 = take((size_t)(L->cap1 > 0 ? L->cap1 : 1) * 12);
+        L->n1 = take(4);
+        L->wl2 = take((size_t)(L->cap2 > 0 ? L->cap2 : 1) * 12);
+        L->n2 = take(4);
+    }
     L->act = take((size_t)act_bytes);
     L->y2 = take((size_t)y2_bytes);
     L->total = off;
@@ -243,7 +249,7 @@ int qmoe_group(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int
     timer_begin(QMOE_STAGE_GROUP, s);
     const hipError_t e = qmoe::launch_group(topk_ids, (int)R, E, m_tile, (int)ceil_div(N, n_tile),
                                             expert_offsets, sorted_routes, worklist,
-                                            worklist_capacity, n_items, 0, nullptr, 0, nullptr, 0, s);
+                                            worklist_capacity, n_items, 0, nullptr, 0, nullptr, s);
     timer_end(QMOE_STAGE_GROUP, s);
     return e == hipSuccess ? ok() : hip_fail(e, "group launch");
 }
@@ -317,16 +323,24 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
 
-    timer_begin(QMOE_STAGE_ROUTE, s);
-    e = qmoe::launch_route(logits, T, E, top_k, normalize, ids, w, s);
-    timer_end(QMOE_STAGE_ROUTE, s);
-    if (e != hipSuccess) return hip_fail(e, "route launch");
+    if (L.decode) {  // routing, grouping and the m-tile list in one launch
+        timer_begin(QMOE_STAGE_ROUTE, s);
+        e = qmoe::launch_decode_plan(logits, (int)T, E, top_k, normalize, w, topk_ids_out,
+                                     topk_w_out, wl1, n1, s);
+        timer_end(QMOE_STAGE_ROUTE, s);
+        if (e != hipSuccess) return hip_fail(e, "decode plan launch");
+    } else {
+        timer_begin(QMOE_STAGE_ROUTE, s);
+        e = qmoe::launch_route(logits, T, E, top_k, normalize, ids, w, s);
+        timer_end(QMOE_STAGE_ROUTE, s);
+        if (e != hipSuccess) return hip_fail(e, "route launch");
 
-    timer_begin(QMOE_STAGE_GROUP, s);
-    e = qmoe::launch_group(ids, (int)R, E, L.m_tile, L.nt1, offsets, sorted, wl1, L.cap1, n1, L.nt2,
-                           wl2, L.cap2, n2, L.decode ? top_k : 0, s);
-    timer_end(QMOE_STAGE_GROUP, s);
-    if (e != hipSuccess) return hip_fail(e, "group launch");
+        timer_begin(QMOE_STAGE_GROUP, s);
+        e = qmoe::launch_group(ids, (int)R, E, L.m_tile, L.nt1, offsets, sorted, wl1, L.cap1, n1,
+                               L.nt2, wl2, L.cap2, n2, s);
+        timer_end(QMOE_STAGE_GROUP, s);
+        if (e != hipSuccess) return hip_fail(e, "group launch");
+    }
 
     qmoe::ProjLaunch p1{};
     p1.a = hidden;
@@ -370,11 +384,11 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     timer_end(QMOE_STAGE_COMBINE, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
 
-    if (topk_ids_out) {
+    if (!L.decode && topk_ids_out) {
         e = hipMemcpyAsync(topk_ids_out, ids, (size_t)R * 4, hipMemcpyDeviceToDevice, s);
         if (e != hipSuccess) return hip_fail(e, "copy topk_ids");
     }
-    if (topk_w_out) {
+    if (!L.decode && topk_w_out) {
         e = hipMemcpyAsync(topk_w_out, w, (size_t)R * 4, hipMemcpyDeviceToDevice, s);
         if (e != hipSuccess) return hip_fail(e, "copy topk_weights");
     }

@@ -25,11 +25,14 @@ constexpr int kPrefillFc2Cols = kPrefillWeightRows;
 constexpr int kDecodeFc1Cols = kDecodeFc1Blocks * 16 / 2;
 constexpr int kDecodeFc2Cols = kDecodeFc2Blocks * 16;
 
-// Decode work-list items carry everything a workgroup needs in one scalar
-// fetch: {expert, n_tile, first sorted row, rows, ids[16]} where ids are the
-// rows' token ids (fc1 list) or route ids (fc2 list), 0 past `rows`.
-constexpr int kDecodeItemInts = 20;
-constexpr int kDecodeMaxRoutes = 128;  // LDS copy of the sorted routes in the group kernel
+// Decode m-tiles carry everything a workgroup needs in one scalar fetch:
+// {expert, first sorted row, rows, 0, token ids[16], route ids[16]}, 0 past
+// `rows`.  Item i of a decode projection with nt column blocks is tile
+// i / nt, column block i % nt.
+constexpr int kDecodeTileInts = 4 + 2 * kDecodeMT;
+constexpr int kDecodeTileTokens = 4;               // first token id
+constexpr int kDecodeTileRoutes = 4 + kDecodeMT;   // first route id
+constexpr int kDecodeMaxRoutes = 128;  // routes the fused decode plan holds in LDS
 
 struct ProjArgs {
     const uint8_t* codes;
@@ -50,8 +53,8 @@ struct ProjLaunch {
     int top_k;
     const int32_t* offsets;   // [E+1]
     const int32_t* sorted;    // [R]
-    const int32_t* worklist;  // [cap, 3]
-    const int32_t* n_items;   // [1]
+    const int32_t* worklist;  // prefill: [cap, 3] triples; decode: m-tiles
+    const int32_t* n_items;   // prefill: [1] items; decode: [1] m-tiles
     int64_t grid;             // workgroups to launch (>= 1)
     int act;                  // fc1 only
     void* act_out;            // fc1: dtype [R, I] in sorted order
@@ -61,11 +64,15 @@ struct ProjLaunch {
 hipError_t launch_route(const float* logits, int64_t T, int E, int top_k, int normalize,
                         int32_t* ids, float* weights, hipStream_t s);
 
-// rich_top_k > 0: decode lists of kDecodeItemInts-int items (m_tile must be
-// kDecodeMT and R <= kDecodeMaxRoutes); 0: {expert, m, n} triples.
 hipError_t launch_group(const int32_t* ids, int R, int E, int m_tile, int nt1, int32_t* offsets,
                         int32_t* sorted, int32_t* wl1, int64_t cap1, int32_t* n1, int nt2,
-                        int32_t* wl2, int64_t cap2, int32_t* n2, int rich_top_k, hipStream_t s);
+                        int32_t* wl2, int64_t cap2, int32_t* n2, hipStream_t s);
+
+// Routing plus the decode m-tile list in one workgroup (T*top_k <=
+// kDecodeMaxRoutes).  ids_out / w_out may be NULL.
+hipError_t launch_decode_plan(const float* logits, int T, int E, int top_k, int normalize,
+                              float* weights, int32_t* ids_out, float* w_out, int32_t* tiles,
+                              int32_t* n_tiles, hipStream_t s);
 
 hipError_t launch_fc1_prefill(const ProjLaunch& p, int dtype, hipStream_t s);
 hipError_t launch_fc2_prefill(const ProjLaunch& p, int dtype, hipStream_t s);

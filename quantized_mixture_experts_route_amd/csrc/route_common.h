@@ -1,0 +1,103 @@
+// route_common.h -- top-k selection of one token by one wavefront, shared by
+// the stand-alone router and the fused decode plan.
+//
+// [qmoe.rs, total_order_key / route_value_is_better / qmoe_route]: experts
+// are ranked by a total-order integer key of the float32 logit bits, equal
+// keys going to the lower expert index; weights are exp(l - m) over the
+// selected experts divided by their sum (normalize) or by the sum over all
+// experts, m being the largest non-NaN logit.
+//
+// Each lane holds EPL experts (lane + 64 j) as 64-bit words (key in the high
+// half, bitwise-inverted expert index in the low half), so one unsigned max
+// picks the highest key and, among equal keys, the lowest index.  k rounds
+// of a lane-local max plus a wave max (ds_swizzle + readlane) select the
+// experts; the winner's word is cleared to 0, below any live word.
+#pragma once
+
+#include "qmoe_device.h"
+
+namespace qmoe {
+
+// Signed total-order key: negative floats get their magnitude bits flipped.
+__device__ inline int32_t route_key(float v)
+{
+    const int32_t b = __builtin_bit_cast(int32_t, v);
+    return b < 0 ? (b ^ 0x7fffffff) : b;
+}
+
+__device__ inline float key_to_logit(int32_t key)
+{
+    return __builtin_bit_cast(float, key < 0 ? (key ^ 0x7fffffff) : key);
+}
+
+// Routes the token whose E logits start at `row`; the whole wavefront calls
+// it.  For every slot s < top_k exactly one lane calls emit(s, expert, weight).
+template <int EPL, class Emit>
+__device__ inline void route_token(const float* row, int E, int top_k, int normalize, Emit emit)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    uint64_t cand[EPL];
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+        const int e = lane + kWave * j;
+        cand[j] = 0;
+        if (e < E) {
+            const float v = row[e];
+            const uint32_t ukey = (uint32_t)route_key(v) ^ 0x80000000u;
+            cand[j] = ((uint64_t)ukey << 32) | (uint32_t)~(uint32_t)e;
+            if (v > m) {
+                m = v;  // NaN compares false and is skipped
+            }
+        }
+    }
+    m = wave_max_f32(m);
+
+    int32_t my_id[EPL];
+    float my_num[EPL];
+    float den = 0.0f;
+    for (int s = 0; s < top_k; ++s) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            best = max_u64(best, cand[j]);
+        }
+        best = wave_max_u64(best);
+        const int e = (int)~(uint32_t)best;
+        const float v = key_to_logit((int32_t)((uint32_t)(best >> 32) ^ 0x80000000u));
+        const float num = expf(v - m);
+        if (normalize) {
+            den += num;  // slot order
+        }
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            if (lane + kWave * j == e) {
+                cand[j] = 0;
+            }
+            if (lane + kWave * j == s) {
+                my_id[j] = e;
+                my_num[j] = num;
+            }
+        }
+    }
+    if (!normalize) {
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lane + kWave * j;
+            if (e < E) {
+                part += expf(row[e] - m);
+            }
+        }
+        den = wave_sum_f32(part);
+    }
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+        const int s = lane + kWave * j;
+        if (s < top_k) {
+            emit(s, my_id[j], my_num[j] / den);
+        }
+    }
+}
+
+}  // namespace qmoe
