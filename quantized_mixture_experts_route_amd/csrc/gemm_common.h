@@ -25,7 +25,7 @@ struct WeightRow {
     int bits;
 
     // byte of the zero-point row holding block blk's value
-    __device__ uint32_t zp_byte(int blk) const { return zp[bits == 3 ? blk : blk / (8 / bits)]; }
+    __device__ uint32_t zp_byte(int blk) const { return zp[bits == 3 ? blk : blk >> (bits == 2 ? 2 : 1)]; }
 };
 
 __device__ inline WeightRow weight_row(const ProjArgs& w, int64_t row, int K, int block_size)
@@ -58,7 +58,7 @@ template <int ZP>
 __device__ inline RawParams load_params(const WeightRow& r, int kk, int block_size)
 {
     RawParams q;
-    q.blk = kk / block_size;
+    q.blk = kk >> __builtin_ctz((unsigned)block_size);  // block_size is a power of two
     q.scale = r.scales[q.blk];
     q.zp = 0;
     if constexpr (ZP == kZpTensor) q.zp = r.zp_byte(q.blk);

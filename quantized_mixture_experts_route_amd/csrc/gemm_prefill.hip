@@ -1,17 +1,32 @@
 // gemm_prefill.hip -- grouped projection for many routed rows per expert.
 //
-// One workgroup (4 wavefronts) takes one work-list item {expert, m, n}: up to
-// kPrefillMT routed rows of that expert against 256 weight rows, each
-// wavefront owning 64 weight rows (4 MFMA column blocks of 16) for all the
-// item's rows.  Packed codes stream from HBM straight into registers, are
-// dequantized there as (code - zp) * scale and fed to bf16/fp16 MFMA; the
-// A rows (gathered hidden states for fc1, sorted activations for fc2) are
-// staged per K super-step in a double-buffered LDS tile shared by the four
-// wavefronts, already permuted to the MFMA register order, while the next
-// super-step's A rows and packed spans are in flight.
+// A workgroup of MT/16 wavefronts takes one work-list item: up to MT routed
+// rows of one expert against 4*MT weight rows, each wavefront owning 64
+// weight rows (4 MFMA column blocks of 16) for all MT rows, so each weight
+// element is dequantized once per MT rows.  Every thread stages exactly one
+// 32-value A span per K super-step, and a wavefront keeps within 256
+// registers, so two wavefronts share each SIMD and one hides the other's
+// waits.  MT = 128 (8 wavefronts, 512 weight rows, one workgroup per CU) for
+// large layers; MT = 64 (4 wavefronts, 256 weight rows, two per CU) when the
+// large tile leaves too few items, and for 16-input blocks and generic zero
+// points, whose extra registers only fit the small tile.
+//
+// Packed codes stream from HBM straight into registers, are dequantized there
+// as (code - zp) * scale and fed to bf16/fp16 MFMA; the A rows (gathered
+// hidden states for fc1, sorted activations for fc2) are staged per K
+// super-step in a double-buffered LDS tile shared by the wavefronts, already
+// permuted to the MFMA register order, while the next super-step's A rows and
+// packed spans are in flight.
 // [PR 32198: weights stay packed in HBM and are dequantized in registers
 // inside the GEMM; gemm_quant_moe.rs, moe_fp8_grouped_gemm: workgroups stride
 // over a compacted work-list, rows addressed through sorted route ids.]
+//
+// Item order: the work-list enumerates (expert, m-tile, n-tile) with n inner;
+// the kernel walks each expert's items with m inner instead, so the m-tiles
+// that share a block of weight rows run back to back, and maps workgroup ids
+// so that consecutive items land on the same XCD (workgroups are dealt to the
+// 8 XCDs round-robin): the weight block is then fetched from HBM once and
+// re-read from that XCD's L2.
 //
 // fc1 (+ activation): a wavefront's 4 column blocks are the gate rows 2j and
 // the up rows 2j+1 of 32 activation columns, arranged so that gate and up of
@@ -24,17 +39,21 @@
 namespace qmoe {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kPitch = kSuperK / 2 + 4;  // LDS row pitch in 32-bit words (64 data + 4 pad)
+constexpr int kXcds = 8;
 
-template <int DT, int BITS, bool FC1, int MT, int ZP>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(ProjLaunch p)
+// TWO: block_size 16, so the two halves of a 32-code span have their own
+// scale and zero point.
+template <int DT, int BITS, bool FC1, int MT, int ZP, bool TWO>
+__global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
 {
     constexpr Order O = code_order<DT, BITS>();
     constexpr int MB = MT / 16;
-    constexpr int kChunks = MT * 4 / kThreads;  // (row, lane-group span) pieces staged per thread
+    constexpr int kThreads = MT * 4;        // one (row, lane-group span) per thread
+    constexpr int kRows = MT * 4;           // weight rows per item (64 per wavefront)
     __shared__ __attribute__((aligned(16))) uint32_t a_lds[2][MT * kPitch];
-    __shared__ int row_src[MT];
+    __shared__ int row_src[MT];  // A row of tile row i
+    __shared__ int row_dst[MT];  // fc2: y2 row (route id) of tile row i
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -44,67 +63,92 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(ProjLaunch p)
     const int K = p.K;
     const int n_super = K / kSuperK;
     const int n_items = *p.n_items;
-    const bool two_blocks = p.block_size < 32;
     const uint16_t* a_src = reinterpret_cast<const uint16_t*>(p.a);
+    const uint32_t row_bytes = (uint32_t)K * BITS / 8;
+    const uint32_t n_blocks = (uint32_t)(K / p.block_size);
+    const uint32_t zp_bytes = BITS == 3 ? n_blocks : (n_blocks + 8 / BITS - 1) / (8 / BITS);
+    const int bs_shift = __builtin_ctz((unsigned)p.block_size);  // block_size is a power of two
+    const int nt = FC1 ? (p.N / 2 + kRows / 2 - 1) / (kRows / 2) : (p.N + kRows - 1) / kRows;
+    const int G = gridDim.x;  // a multiple of kXcds
+    const int vb = (int)(blockIdx.x % kXcds) * (G / kXcds) + (int)(blockIdx.x / kXcds);
 
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    for (int item = vb; item < n_items; item += G) {
         const int e = p.worklist[3 * item + 0];
-        const int mt = p.worklist[3 * item + 1];
-        const int nt = p.worklist[3 * item + 2];
-        const int row0 = p.offsets[e] + mt * MT;
-        const int rows = min(MT, p.offsets[e + 1] - row0);
+        const int local0 = p.worklist[3 * item + 1] * nt + p.worklist[3 * item + 2];
+        const int first = p.offsets[e];
+        const int count = p.offsets[e + 1] - first;
+        const int mt_e = (count + MT - 1) / MT;
+        const int mt = local0 % mt_e;  // m inner
+        const int ntile = local0 / mt_e;
+        const int row0 = first + mt * MT;
+        const int rows = min(MT, count - mt * MT);
 
+        // weight rows of this wavefront as 32-bit offsets from the expert's
+        // (uniform) bases; a wavefront past the last column (partial n-tile)
+        // reads the expert's first rows and stores nothing
         int col0;  // fc1: first activation column of this wave; fc2: first hidden column
         bool active;
-        WeightRow wr[4];
+        uint32_t wrow[4];  // weight row within the expert
         if constexpr (FC1) {
-            col0 = nt * kPrefillFc1Cols + wave * 32;
+            col0 = ntile * (kRows / 2) + wave * 32;
             active = col0 < p.N / 2;
-            const int64_t base = (int64_t)e * p.N + (active ? 2 * (col0 + c) : 0);
-            wr[0] = weight_row(p.w, base, K, p.block_size);
-            wr[1] = weight_row(p.w, base + 1, K, p.block_size);
-            wr[2] = weight_row(p.w, base + (active ? 32 : 0), K, p.block_size);
-            wr[3] = weight_row(p.w, base + (active ? 33 : 1), K, p.block_size);
+            const uint32_t base = active ? 2 * (col0 + c) : 0;
+            wrow[0] = base;
+            wrow[1] = base + 1;
+            wrow[2] = base + (active ? 32 : 0);
+            wrow[3] = base + (active ? 33 : 1);
         } else {
-            col0 = nt * kPrefillFc2Cols + wave * 64;
+            col0 = ntile * kRows + wave * 64;
             active = col0 < p.N;
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                wr[nb] = weight_row(p.w, (int64_t)e * p.N + (active ? col0 + nb * 16 + c : 0), K,
-                                    p.block_size);
-            }
+            for (int nb = 0; nb < 4; ++nb) wrow[nb] = active ? col0 + nb * 16 + c : 0;
         }
+        const int64_t erow = (int64_t)e * p.N;
+        const uint8_t* codes_e = p.w.codes + erow * row_bytes;
+        const uint16_t* scales_e = reinterpret_cast<const uint16_t*>(p.w.scales) + erow * n_blocks;
+        const uint8_t* zp_e = ZP == kZpTensor ? p.w.zp + erow * zp_bytes : nullptr;
 
         __syncthreads();  // the previous item is done with row_src and a_lds
         for (int i = tid; i < MT; i += kThreads) {
-            int src = -1;
-            if (i < rows) src = FC1 ? p.sorted[row0 + i] / p.top_k : row0 + i;
-            row_src[i] = src;
+            // rows past the tile repeat its first row: their outputs are never stored
+            const int r = i < rows ? i : 0;
+            const int route = p.sorted[row0 + r];
+            row_src[i] = FC1 ? route / p.top_k : row0 + r;
+            row_dst[i] = route;
         }
         __syncthreads();
 
-        uint32_t a_stage[kChunks][16];
-        Span<BITS> sp[4];
-        RawParams bp[4];
-        auto load_step = [&](int s) {
-            const int k0 = s * kSuperK;
+        // this thread's A span: row tid/4, inputs [32*(tid%4), +32) of a super-step
+        const uint16_t* a_ptr = a_src + (int64_t)row_src[tid >> 2] * K + 32 * (tid & 3);
+        uint32_t a_stage[16];
+        auto load_a = [&](int s) { load_a_span(a_ptr, s * kSuperK, a_stage); };
+        auto store_a = [&](uint32_t* buf) {
+            uint32_t perm[16];
+            permute_span<O>(a_stage, perm);
+            uint32_t* dst = buf + (tid >> 2) * kPitch + 16 * (tid & 3);
 #pragma unroll
-            for (int j = 0; j < kChunks; ++j) {
-                const int q = tid + kThreads * j;
-                const int src = row_src[q >> 2];
-                if (src >= 0) {
-                    load_a_span(a_src + (int64_t)src * K, k0 + 32 * (q & 3), a_stage[j]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) a_stage[j][i] = 0u;
-                }
+            for (int v = 0; v < 4; ++v) {
+                *reinterpret_cast<u32x4*>(dst + 4 * v) =
+                    u32x4{perm[4 * v], perm[4 * v + 1], perm[4 * v + 2], perm[4 * v + 3]};
             }
-            if (active) {
+        };
+        // scale and zero-point byte of the block holding input kk of row nb
+        auto params = [&](int nb, int kk) {
+            RawParams q;
+            q.blk = kk >> bs_shift;
+            q.scale = scales_e[wrow[nb] * n_blocks + q.blk];
+            q.zp = 0;
+            if constexpr (ZP == kZpTensor) {
+                q.zp = zp_e[wrow[nb] * zp_bytes + (BITS == 3 ? q.blk : q.blk >> (BITS == 2 ? 2 : 1))];
+            }
+            return q;
+        };
+        auto load_b = [&](int s, Span<BITS> (&sp)[4], RawParams (&bp)[4]) {
+            const int kk = s * kSuperK + 32 * g;
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    sp[nb] = load_span<BITS>(wr[nb].codes, k0 + 32 * g);
-                    bp[nb] = load_params<ZP>(wr[nb], k0 + 32 * g, p.block_size);
-                }
+            for (int nb = 0; nb < 4; ++nb) {
+                sp[nb] = load_span<BITS>(codes_e + wrow[nb] * row_bytes, kk);
+                bp[nb] = params(nb, kk);
             }
         };
 
@@ -114,21 +158,37 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(ProjLaunch p)
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        load_step(0);
-        for (int s = 0; s < n_super; ++s) {
-            uint32_t* buf = a_lds[s & 1];
+        auto compute = [&](const uint32_t* buf, const Span<BITS> (&cur)[4], const RawParams (&cbp)[4],
+                           int s) {
+            const int kk = s * kSuperK + 32 * g;
 #pragma unroll
-            for (int j = 0; j < kChunks; ++j) {
-                const int q = tid + kThreads * j;
-                uint32_t perm[16];
-                permute_span<O>(a_stage[j], perm);
-                uint32_t* dst = buf + (q >> 2) * kPitch + 16 * (q & 3);
+            for (int t = 0; t < 4; ++t) {
+                u32x4 bf[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    *reinterpret_cast<u32x4*>(dst + 4 * v) =
-                        u32x4{perm[4 * v], perm[4 * v + 1], perm[4 * v + 2], perm[4 * v + 3]};
+                for (int nb = 0; nb < 4; ++nb) {
+                    const RawParams rq = (TWO && t >= 2) ? params(nb, kk + 16) : cbp[nb];
+                    const BlockParams q = decode_params<DT, BITS, ZP>(rq, p.w.zp_fallback);
+                    bf[nb] = dequant_zp<DT, BITS, ZP>(cur[nb], t, q);
+                }
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const u32x4 af = *reinterpret_cast<const u32x4*>(
+                        buf + (mb * 16 + c) * kPitch + 16 * g + 4 * t);
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) {
+                        acc[mb][nb] = Dt<DT>::mfma(af, bf[nb], acc[mb][nb]);
+                    }
                 }
             }
+        };
+
+        Span<BITS> sp[4];
+        RawParams bp[4];
+        load_a(0);
+        load_b(0, sp, bp);
+        for (int s = 0; s < n_super; ++s) {
+            uint32_t* buf = a_lds[s & 1];
+            store_a(buf);
             Span<BITS> cur[4];
             RawParams cbp[4];
 #pragma unroll
@@ -137,34 +197,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(ProjLaunch p)
                 cbp[nb] = bp[nb];
             }
             __syncthreads();
-            if (s + 1 < n_super) load_step(s + 1);  // in flight during the MFMAs below
-
-            if (active) {
-                const int kk = s * kSuperK + 32 * g;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    u32x4 bf[4];
-#pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) {
-                        const RawParams rq = (two_blocks && t >= 2)
-                                                 ? load_params<ZP>(wr[nb], kk + 16, p.block_size)
-                                                 : cbp[nb];
-                        const BlockParams q = decode_params<DT, BITS, ZP>(rq, p.w.zp_fallback);
-                        bf[nb] = dequant_zp<DT, BITS, ZP>(cur[nb], t, q);
-                    }
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        if (mb * 16 < rows) {
-                            const u32x4 af = *reinterpret_cast<const u32x4*>(
-                                buf + (mb * 16 + c) * kPitch + 16 * g + 4 * t);
-#pragma unroll
-                            for (int nb = 0; nb < 4; ++nb) {
-                                acc[mb][nb] = Dt<DT>::mfma(af, bf[nb], acc[mb][nb]);
-                            }
-                        }
-                    }
-                }
+            if (s + 1 < n_super) {  // in flight during the MFMAs below
+                load_a(s + 1);
+                load_b(s + 1, sp, bp);
             }
+            compute(buf, cur, cbp, s);
         }
 
         if (!active) continue;
@@ -181,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(ProjLaunch p)
                     out[col0 + 16 + c] =
                         Dt<DT>::from_float(act_value<DT>(p.act, acc[mb][2][i], acc[mb][3][i]));
                 } else {
-                    float* out = p.y2 + (int64_t)p.sorted[row0 + m] * p.N;
+                    float* out = p.y2 + (int64_t)row_dst[m] * p.N;
 #pragma unroll
                     for (int nb = 0; nb < 4; ++nb) out[col0 + nb * 16 + c] = acc[mb][nb][i];
                 }
@@ -190,40 +227,89 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(ProjLaunch p)
     }
 }
 
-template <bool FC1, int DT, int BITS>
-hipError_t launch_zp(const ProjLaunch& p, hipStream_t s)
+// Compute units of the current device (cached per device).
+int device_cus()
 {
-    const dim3 grid((unsigned)p.grid), block(kThreads);
-    constexpr int MT = kPrefillMT;
-    switch (zp_mode(p.w)) {
-    case kZpConst: hipLaunchKernelGGL((prefill_kernel<DT, BITS, FC1, MT, kZpConst>), grid, block, 0, s, p); break;
-    case kZpTensor: hipLaunchKernelGGL((prefill_kernel<DT, BITS, FC1, MT, kZpTensor>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((prefill_kernel<DT, BITS, FC1, MT, kZpGeneric>), grid, block, 0, s, p); break;
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        hipDeviceProp_t prop;
+        cus[dev] = hipGetDeviceProperties(&prop, dev) == hipSuccess ? prop.multiProcessorCount : 256;
     }
+    return cus[dev];
+}
+
+// Persistent grid: as many workgroups as are resident at once (never more
+// than the item bound), rounded up to a multiple of the XCD count.
+template <class Kernel>
+int64_t persistent_grid(Kernel kernel, int threads, int64_t item_bound)
+{
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+        per_cu < 1) {
+        per_cu = 1;
+    }
+    int64_t g = (int64_t)device_cus() * per_cu;
+    if (item_bound < g) g = item_bound;
+    return (g + kXcds - 1) / kXcds * kXcds;
+}
+
+template <bool FC1, int DT, int BITS, int MT, int ZP>
+hipError_t launch_one(const ProjLaunch& p, hipStream_t s)
+{
+    auto kernel = p.block_size < 32 ? prefill_kernel<DT, BITS, FC1, MT, ZP, true>
+                                    : prefill_kernel<DT, BITS, FC1, MT, ZP, false>;
+    const int64_t grid = persistent_grid(kernel, MT * 4, p.grid > 0 ? p.grid : 1);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(MT * 4), 0, s, p);
     return hipGetLastError();
 }
 
-template <bool FC1, int DT>
-hipError_t launch_dt(const ProjLaunch& p, hipStream_t s)
+template <bool FC1, int DT, int BITS, int MT>
+hipError_t launch_zp(const ProjLaunch& p, hipStream_t s)
+{
+    switch (zp_mode(p.w)) {
+    case kZpConst: return launch_one<FC1, DT, BITS, MT, kZpConst>(p, s);
+    case kZpTensor: return launch_one<FC1, DT, BITS, MT, kZpTensor>(p, s);
+    default: return launch_one<FC1, DT, BITS, MT, kZpGeneric>(p, s);
+    }
+}
+
+template <bool FC1, int DT, int MT>
+hipError_t launch_bits(const ProjLaunch& p, hipStream_t s)
 {
     switch (p.w.bits) {
-    case 2: return launch_zp<FC1, DT, 2>(p, s);
-    case 3: return launch_zp<FC1, DT, 3>(p, s);
-    case 4: return launch_zp<FC1, DT, 4>(p, s);
+    case 2: return launch_zp<FC1, DT, 2, MT>(p, s);
+    case 3: return launch_zp<FC1, DT, 3, MT>(p, s);
+    case 4: return launch_zp<FC1, DT, 4, MT>(p, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <bool FC1>
+hipError_t launch_prefill(const ProjLaunch& p, int dtype, hipStream_t s)
+{
+    if (p.m_tile == kPrefillMTLarge) {
+        return dtype == kBF16 ? launch_bits<FC1, kBF16, kPrefillMTLarge>(p, s)
+                              : launch_bits<FC1, kF16, kPrefillMTLarge>(p, s);
+    }
+    if (p.m_tile == kPrefillMTSmall) {
+        return dtype == kBF16 ? launch_bits<FC1, kBF16, kPrefillMTSmall>(p, s)
+                              : launch_bits<FC1, kF16, kPrefillMTSmall>(p, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_fc1_prefill(const ProjLaunch& p, int dtype, hipStream_t s)
 {
-    return dtype == kBF16 ? launch_dt<true, kBF16>(p, s) : launch_dt<true, kF16>(p, s);
+    return launch_prefill<true>(p, dtype, s);
 }
 
 hipError_t launch_fc2_prefill(const ProjLaunch& p, int dtype, hipStream_t s)
 {
-    return dtype == kBF16 ? launch_dt<false, kBF16>(p, s) : launch_dt<false, kF16>(p, s);
+    return launch_prefill<false>(p, dtype, s);
 }
 
 }  // namespace qmoe

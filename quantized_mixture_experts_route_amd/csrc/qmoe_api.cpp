@@ -88,7 +88,10 @@ struct Layout {
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L)
+// prefill_mt: the prefill tile rows to lay the work-lists out for; the small
+// tile (the default) yields the most items, so its layout bounds the others.
+bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L,
+                 int prefill_mt = qmoe::kPrefillMTSmall)
 {
     int64_t R;
     if (T < 0 || H <= 0 || I <= 0 || E <= 0 || top_k <= 0 || !mul_ok(T, top_k, &R) ||
@@ -96,9 +99,9 @@ bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L)
         return false;
     }
     L->decode = R <= QMOE_DECODE_MAX_ROUTES;
-    L->m_tile = L->decode ? qmoe::kDecodeMT : qmoe::kPrefillMT;
-    const int fc1_cols = L->decode ? qmoe::kDecodeFc1Cols : qmoe::kPrefillFc1Cols;
-    const int fc2_cols = L->decode ? qmoe::kDecodeFc2Cols : qmoe::kPrefillFc2Cols;
+    L->m_tile = L->decode ? qmoe::kDecodeMT : prefill_mt;
+    const int fc1_cols = L->decode ? qmoe::kDecodeFc1Cols : qmoe::prefill_fc1_cols(L->m_tile);
+    const int fc2_cols = L->decode ? qmoe::kDecodeFc2Cols : qmoe::prefill_fc2_cols(L->m_tile);
     L->nt1 = (int)ceil_div(I, fc1_cols);
     L->nt2 = (int)ceil_div(H, fc2_cols);
     const int64_t m_tiles = ceil_div(R, L->m_tile) + (E < R ? E : R);
@@ -294,6 +297,14 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     Layout L;
     if (!make_layout(T, H, I, E, top_k, &L)) return fail(QMOE_ERR_INVALID_ARG, "sizes overflow");
     if (T == 0) return ok();
+    // the large prefill tile when its registers fit (block_size >= 32, fast
+    // zero points) and it still yields a few items per CU
+    const qmoe::ProjArgs w1 = proj_args(fc1, zero_point_offset);
+    const qmoe::ProjArgs w2 = proj_args(fc2, zero_point_offset);
+    if (!L.decode && block_size >= 32 && w1.fast && w2.fast &&
+        (T * top_k / qmoe::kPrefillMTLarge) * ceil_div(I, qmoe::prefill_fc1_cols(qmoe::kPrefillMTLarge)) >= 1024) {
+        make_layout(T, H, I, E, top_k, &L, qmoe::kPrefillMTLarge);
+    }
     if (!hidden || !logits || !out) return fail(QMOE_ERR_INVALID_ARG, "hidden, logits and out must be non-NULL");
     if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(logits, 4)) {
         return fail(QMOE_ERR_INVALID_ARG, "hidden/out must be 16-byte and logits 4-byte aligned");
@@ -344,11 +355,12 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
 
     qmoe::ProjLaunch p1{};
     p1.a = hidden;
-    p1.w = proj_args(fc1, zero_point_offset);
+    p1.w = w1;
     p1.K = H;
     p1.N = 2 * I;
     p1.block_size = block_size;
     p1.top_k = top_k;
+    p1.m_tile = L.m_tile;
     p1.offsets = offsets;
     p1.sorted = sorted;
     p1.worklist = wl1;
@@ -363,11 +375,12 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
 
     qmoe::ProjLaunch p2{};
     p2.a = act;
-    p2.w = proj_args(fc2, zero_point_offset);
+    p2.w = w2;
     p2.K = I;
     p2.N = H;
     p2.block_size = block_size;
     p2.top_k = top_k;
+    p2.m_tile = L.m_tile;
     p2.offsets = offsets;
     p2.sorted = sorted;
     p2.worklist = wl2;

@@ -162,8 +162,7 @@ enum class Order { kNatural, kStride4, kStride8 };
 template <int DT, int BITS>
 __host__ __device__ constexpr Order code_order()
 {
-    if (DT == kF16) return BITS == 2 ? Order::kStride8 : Order::kStride4;
-    return BITS == 3 ? Order::kStride4 : Order::kNatural;
+    return BITS == 2 ? Order::kStride8 : Order::kStride4;
 }
 
 __host__ __device__ constexpr int order_lo(Order o, int t, int r)
@@ -227,12 +226,14 @@ __host__ __device__ inline bool zp_is_half_integer(float zp)
 // [PR 33569: dequantized weights are rounded to the activation type before
 // accumulation].
 //
-// fp16: a code placed at mantissa bits 1.. of 0x6000 (512.0, spacing 0.5)
-// reads as 512 + code; subtracting 512 + zp is exact for half-integer zp, and
-// the packed multiply by the fp16 scale rounds once.
-// bf16: codes spread one per byte convert with v_cvt_f32_ubyte, one fma forms
-// code*s - zp*s = (code - zp)*s exactly in float32 (zp*s is exact for
-// half-integer zp and a 16-bit scale), v_cvt_pk_bf16_f32 rounds once.
+// Both dtypes first place each code at mantissa bits 1.. of the fp16 value
+// 0x6000 (512.0, spacing 0.5), so the register reads as the fp16 pair
+// (512 + code, 512 + code').
+// fp16: subtracting 512 + zp is exact for half-integer zp, and the packed
+// multiply by the fp16 scale rounds once.
+// bf16: v_fma_mix_f32 forms (512 + code)*s - (512 + zp)*s from the fp16
+// halves; both terms are exact in float32 (at most 11 + 8 significant bits),
+// so the result is (code - zp)*s exactly and v_cvt_pk_bf16_f32 rounds once.
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // A loop-invariant value the compiler must keep in a register (VGPR or
@@ -260,73 +261,54 @@ __device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic)
 template <int DT, int BITS>
 __device__ inline u32x4 dequant_step(const Span<BITS>& sp, int t, float zp, float scale)
 {
+    // codes to fp16 (512 + q): one v_and_or per register (two codes)
+    const uint32_t kMagic = opaque(0x60006000u);
+    uint32_t raw[4];
+    if constexpr (BITS == 4) {
+        const uint32_t g = sp.w[t];
+        raw[0] = and_or(g << 1, 0x001e001eu, kMagic);
+#pragma unroll
+        for (int r = 1; r < 4; ++r) raw[r] = and_or(g >> (4 * r - 1), 0x001e001eu, kMagic);
+    } else if constexpr (BITS == 2) {
+        const uint32_t w = sp.w[t >> 1];
+        const int j0 = 4 * (t & 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = j0 + r;
+            raw[r] = and_or(j == 0 ? (w << 1) : (w >> (2 * j - 1)), 0x00060006u, kMagic);
+        }
+    } else {
+        const uint32_t g = span_group<3>(sp, t);
+        const uint32_t y = (g & 0xfffu) | ((g << 4) & 0x0fff0000u);  // codes 4-7 to bit 16
+        raw[0] = and_or(y << 1, 0x000e000eu, kMagic);
+#pragma unroll
+        for (int r = 1; r < 4; ++r) raw[r] = and_or(y >> (3 * r - 1), 0x000e000eu, kMagic);
+    }
     u32x4 out;
     if constexpr (DT == kF16) {
-        const uint32_t kMagic = opaque(0x60006000u);
+        // (512 + q) - (512 + zp) is exact in fp16 for half-integer zp; one
+        // rounding in the multiply
         const _Float16 c = (_Float16)(-(512.0f + zp));
         const f16x2 c2 = {c, c};
         const _Float16 sh = (_Float16)scale;
         const f16x2 s2 = {sh, sh};
-        uint32_t raw[4];
-        if constexpr (BITS == 4) {
-            const uint32_t g = sp.w[t];
-            raw[0] = and_or(g << 1, 0x001e001eu, kMagic);
-#pragma unroll
-            for (int r = 1; r < 4; ++r) raw[r] = and_or(g >> (4 * r - 1), 0x001e001eu, kMagic);
-        } else if constexpr (BITS == 2) {
-            const uint32_t w = sp.w[t >> 1];
-            const int j0 = 4 * (t & 1);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = j0 + r;
-                raw[r] = and_or(j == 0 ? (w << 1) : (w >> (2 * j - 1)), 0x00060006u, kMagic);
-            }
-        } else {
-            const uint32_t g = span_group<3>(sp, t);
-            const uint32_t y = (g & 0xfffu) | ((g << 4) & 0x0fff0000u);  // codes 4-7 to bit 16
-            raw[0] = and_or(y << 1, 0x000e000eu, kMagic);
-#pragma unroll
-            for (int r = 1; r < 4; ++r) raw[r] = and_or(y >> (3 * r - 1), 0x000e000eu, kMagic);
-        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const f16x2 v = (__builtin_bit_cast(f16x2, raw[r]) + c2) * s2;
             out[r] = __builtin_bit_cast(uint32_t, v);
         }
     } else {
-        const float c = -zp * scale;
-        auto cvt = [&](uint32_t x, int byte) {
-            return __builtin_fmaf((float)((x >> (8 * byte)) & 0xffu), scale, c);
-        };
-        auto pack_bf16 = [](float lo, float hi) {
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            const bf16x2 v = {(__bf16)lo, (__bf16)hi};
-            return __builtin_bit_cast(uint32_t, v);
-        };
-        if constexpr (BITS == 4) {
-            const uint32_t g = sp.w[t];
-            const uint32_t lo = g & 0x0f0f0f0fu, hi = (g >> 4) & 0x0f0f0f0fu;
+        // (512 + q) * s - (512 + zp) * s in one fused multiply-add with fp16
+        // inputs (v_fma_mix_f32): both products are exact in float32, so the
+        // result is (q - zp) * s exactly, rounded once to bf16
+        const float c = -(512.0f + zp) * scale;
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) out[r] = pack_bf16(cvt(lo, r), cvt(hi, r));
-        } else if constexpr (BITS == 2) {
-            const uint32_t w = sp.w[t >> 1];
-            const int h = t & 1;
-            uint32_t b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) b[i] = (w >> (2 * i)) & 0x03030303u;  // code c: byte c/4 of b[c%4]
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int byte = 2 * h + (r >> 1);
-                out[r] = pack_bf16(cvt(b[(r & 1) * 2], byte), cvt(b[(r & 1) * 2 + 1], byte));
-            }
-        } else {
-            const uint32_t g = span_group<3>(sp, t);
-            const uint32_t y = (g & 0xfffu) | ((g << 4) & 0x0fff0000u);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t z = (y >> (3 * r)) & 0x00070007u;  // codes r, r+4 in bytes 0, 2
-                out[r] = pack_bf16(cvt(z, 0), cvt(z, 2));
-            }
+        for (int r = 0; r < 4; ++r) {
+            const f16x2 h = __builtin_bit_cast(f16x2, raw[r]);
+            const bf16x2 v = {(__bf16)__builtin_fmaf((float)h.x, scale, c),
+                              (__bf16)__builtin_fmaf((float)h.y, scale, c)};
+            out[r] = __builtin_bit_cast(uint32_t, v);
         }
     }
     return out;

@@ -7,12 +7,13 @@
 
 namespace qmoe {
 
-// Tile shapes.  Prefill: a workgroup computes kPrefillMT routed rows of one
-// expert against 256 weight rows (4 waves x 4 MFMA column blocks of 16).
-// Decode: a workgroup computes up to 16 rows against kDecodeFc{1,2}Blocks
-// column blocks of 16 weight rows, its 4 waves splitting K.
-constexpr int kPrefillMT = 128;
-constexpr int kPrefillWeightRows = 256;
+// Tile shapes.  Prefill: a workgroup computes MT routed rows of one expert
+// against 4*MT weight rows (MT/16 wavefronts x 64 rows); MT is
+// kPrefillMTLarge or kPrefillMTSmall, chosen per layer call.  Decode: a workgroup computes up
+// to 16 rows against kDecodeFc{1,2}Blocks column blocks of 16 weight rows,
+// its 8 wavefronts splitting K.
+constexpr int kPrefillMTLarge = 128;
+constexpr int kPrefillMTSmall = 64;
 constexpr int kDecodeMT = 16;
 constexpr int kDecodeFc1Blocks = 4;  // 64 weight rows = 32 gate/up pairs
 constexpr int kDecodeFc2Blocks = 2;  // 32 hidden columns
@@ -20,8 +21,8 @@ constexpr int kSuperK = 128;  // inputs per K super-step: 4 lane groups x 32 cod
 
 // Output columns one work-list item covers (fc1 counts activation columns,
 // i.e. gate/up row pairs; fc2 counts hidden columns).
-constexpr int kPrefillFc1Cols = kPrefillWeightRows / 2;
-constexpr int kPrefillFc2Cols = kPrefillWeightRows;
+constexpr int prefill_fc1_cols(int mt) { return 2 * mt; }
+constexpr int prefill_fc2_cols(int mt) { return 4 * mt; }
 constexpr int kDecodeFc1Cols = kDecodeFc1Blocks * 16 / 2;
 constexpr int kDecodeFc2Cols = kDecodeFc2Blocks * 16;
 
@@ -51,11 +52,12 @@ struct ProjLaunch {
     int N;                    // weight rows (fc1: 2*I, fc2: H)
     int block_size;
     int top_k;
+    int m_tile;               // prefill tile rows (kPrefillMTLarge or kPrefillMTSmall)
     const int32_t* offsets;   // [E+1]
     const int32_t* sorted;    // [R]
     const int32_t* worklist;  // prefill: [cap, 3] triples; decode: m-tiles
     const int32_t* n_items;   // prefill: [1] items; decode: [1] m-tiles
-    int64_t grid;             // workgroups to launch (>= 1)
+    int64_t grid;             // decode: workgroups to launch; prefill: item bound
     int act;                  // fc1 only
     void* act_out;            // fc1: dtype [R, I] in sorted order
     float* y2;                // fc2: float32 [R, H] by route id
