@@ -16,6 +16,16 @@ roofline (fc1: packed-weight bytes of the selected experts per launch for
 decode -> GB/s vs 8 TB/s; 2*R*H*2I flops per launch for prefill -> TFLOP/s vs
 2.5 PFLOP/s dense fp16/bf16), and the CPU oracle timed on the host cores on a
 bounded sample as a baseline.
+
+The timed region runs the steps with nothing else on the stream; the fc1
+kernel's average duration comes from a second pass over the same number of
+steps with a HIP event pair around each fc1 launch (on the library's stream),
+so the event overhead does not enter the step time.
+
+--calibrate-copy adds one elementwise kernel of known traffic (neg of a 256
+MiB float32 tensor: 256 MiB read, 256 MiB written) before the timed region,
+for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE; --pmc-summary DIR prints the
+per-kernel averages of the rocprofv3 CSV files under DIR (no GPU use).
 """
 from __future__ import annotations
 
@@ -50,6 +60,12 @@ def _args():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 256 MiB elementwise kernel before the timed region")
+    ap.add_argument("--digest", action="store_true",
+                    help="print the digest of the kernel sources that traffic counters are tied to")
+    ap.add_argument("--pmc-summary", metavar="DIR",
+                    help="summarize rocprofv3 CSV files under DIR and exit")
     ap.add_argument("--stages", action="store_true",
                     help="also time every stage separately after the timed region")
     return ap.parse_args()
@@ -103,8 +119,62 @@ def _cpu_baseline(inp, spec, min_seconds):
             "sample": f"{n_tok} of {T} tokens, {reps} passes, {el:.1f} s, double precision"}
 
 
+CALIBRATION_BYTES = 256 << 20
+
+
+def kernel_source_digest():
+    """sha256 over the library's kernel sources: traffic counters recorded for
+    another digest belong to other kernels and are not reported."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "quantized_mixture_experts_route_amd", "csrc", "*"))):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def _pmc_summary(root):
+    """Per-kernel averages of rocprofv3 counter and kernel-stats CSV files."""
+    import csv
+    import glob
+    from collections import defaultdict
+    def short(name):
+        return name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+    vals = defaultdict(lambda: defaultdict(list))
+    for f in glob.glob(os.path.join(root, "**", "*_counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            vals[short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    for name, counters in sorted(vals.items()):
+        if "rocprim" in name or "fillBuffer" in name:
+            continue
+        avg = {c: sum(v) / len(v) for c, v in counters.items()}
+        print(f"{name}: " + ", ".join(f"{c}={a:.6g} (n={len(counters[c])})" for c, a in avg.items()))
+        if "neg" in name:
+            for c, a in avg.items():
+                if c in ("FETCH_SIZE", "WRITE_SIZE"):
+                    print(f"  calibration {c}: {a * 1024 / CALIBRATION_BYTES:.4f} x bytes moved")
+    for f in glob.glob(os.path.join(root, "**", "*_kernel_stats.csv"), recursive=True):
+        print(f"{f}:")
+        print("| kernel | calls | avg us | min us | max us |\n|---|---|---|---|---|")
+        for r in csv.DictReader(open(f)):
+            if "rocprim" in r["Name"]:
+                continue
+            print(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} "
+                  f"| {float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+
+
 def main():
     a = _args()
+    if a.digest:
+        print(kernel_source_digest())
+        return
+    if a.pmc_summary:
+        _pmc_summary(a.pmc_summary)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
               "(the layer's multi-GPU expert-parallel sharding is a design, not built)",
@@ -133,19 +203,30 @@ def main():
                    block_size=spec["block_size"], normalize=spec["normalize"],
                    activation=spec["act"], zero_point_offset=spec["zpo"], out=out, workspace=ws)
 
+    if a.calibrate_copy:
+        src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
-    qm.timer_start(qm.STAGE_FC1)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    fc1_ms, fc1_n = qm.timer_stop()
     ms_per_step = elapsed * 1e3 / steps
+
+    # fc1 kernel duration: HIP events around each fc1 launch over another
+    # `steps` steps (same weight rotation)
+    qm.timer_start(qm.STAGE_FC1)
+    for i in range(steps):
+        step(warmup + steps + i)
+    fc1_ms, fc1_n = qm.timer_stop()
     fc1_avg_ms = fc1_ms / max(fc1_n, 1)
 
     # algorithmic work of one fc1 launch
@@ -169,7 +250,10 @@ def main():
     if os.path.exists(PROFILE_TRAFFIC):
         with open(PROFILE_TRAFFIC) as f:
             traffic = json.load(f).get(spec["name"])
-    roof["traffic"] = traffic
+    if isinstance(traffic, dict) and traffic.get("kernel_source_sha256") == kernel_source_digest():
+        roof["traffic"] = traffic.get("bytes_per_launch")
+    else:
+        roof["traffic"] = None
 
     result = {
         "metric": METRIC, "value": round(T / (ms_per_step * 1e-3), 2), "unit": "tokens/s",

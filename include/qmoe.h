@@ -186,11 +186,13 @@ int qmoe_dequantize(const qmoe_proj* p, int32_t E, int32_t N, int32_t K, int32_t
 
 /*
  * Kernel timer for measurement.  After qmoe_timer_start(stage), every
- * qmoe_forward call records a HIP event pair on its stream around each
- * launch of that stage's kernel (at most 4096 pairs).  qmoe_timer_stop()
- * waits for the recorded events, stores the summed elapsed milliseconds and
- * the number of launches timed, and disables the timer.
- * Stages: 0 route, 1 group, 2 fc1 (+ activation), 3 fc2, 4 combine.
+ * qmoe_forward call attaches a HIP event pair to the dispatch of that
+ * stage's kernel (hipExtLaunchKernelGGL start/stop events, at most 4096
+ * pairs).  qmoe_timer_stop() waits for the recorded events, stores the summed
+ * elapsed milliseconds and the number of launches timed, and disables the
+ * timer.  Stages: 0 route (on the decode path: routing, grouping and the
+ * m-tile list in one kernel), 1 group (prefill path only), 2 fc1
+ * (+ activation), 3 fc2, 4 combine.
  */
 #define QMOE_STAGE_ROUTE 0
 #define QMOE_STAGE_GROUP 1

@@ -46,9 +46,9 @@ hipError_t launch_combine(const float* y2, const float* weights, int64_t T, int 
     const dim3 grid((unsigned)((n + 255) / 256)), block(256);
     uint16_t* o = reinterpret_cast<uint16_t*>(out);
     if (dtype == kBF16) {
-        hipLaunchKernelGGL(combine_kernel<kBF16>, grid, block, 0, s, y2, weights, T, H, top_k, o);
+        launch(combine_kernel<kBF16>, grid, block, s, y2, weights, T, H, top_k, o);
     } else {
-        hipLaunchKernelGGL(combine_kernel<kF16>, grid, block, 0, s, y2, weights, T, H, top_k, o);
+        launch(combine_kernel<kF16>, grid, block, s, y2, weights, T, H, top_k, o);
     }
     return hipGetLastError();
 }

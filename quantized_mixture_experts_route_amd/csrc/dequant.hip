@@ -47,9 +47,9 @@ hipError_t launch_zp(const ProjArgs& w, int64_t rows, int K, int block_size, int
     const int64_t n = rows * (K / 32);
     const dim3 grid((unsigned)((n + 255) / 256)), block(256);
     switch (zp_mode(w)) {
-    case kZpConst: hipLaunchKernelGGL((dequant_kernel<DT, BITS, kZpConst>), grid, block, 0, s, w, rows, K, block_size, codes_out, w_out); break;
-    case kZpTensor: hipLaunchKernelGGL((dequant_kernel<DT, BITS, kZpTensor>), grid, block, 0, s, w, rows, K, block_size, codes_out, w_out); break;
-    default: hipLaunchKernelGGL((dequant_kernel<DT, BITS, kZpGeneric>), grid, block, 0, s, w, rows, K, block_size, codes_out, w_out); break;
+    case kZpConst: launch(dequant_kernel<DT, BITS, kZpConst>, grid, block, s, w, rows, K, block_size, codes_out, w_out); break;
+    case kZpTensor: launch(dequant_kernel<DT, BITS, kZpTensor>, grid, block, s, w, rows, K, block_size, codes_out, w_out); break;
+    default: launch(dequant_kernel<DT, BITS, kZpGeneric>, grid, block, s, w, rows, K, block_size, codes_out, w_out); break;
     }
     return hipGetLastError();
 }

@@ -270,8 +270,8 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(ProjLaunch p,
 template <bool FC1, int DT, int NB, int BITS, int ZP, bool RAW, bool STAGED = false>
 hipError_t launch_one(const ProjLaunch& p, hipStream_t s)
 {
-    hipLaunchKernelGGL((decode_kernel<DT, BITS, FC1, NB, ZP, RAW, STAGED>), dim3((unsigned)p.grid),
-                       dim3(kThreads), 0, s, p, p.worklist, p.n_items);
+    launch(decode_kernel<DT, BITS, FC1, NB, ZP, RAW, STAGED>, dim3((unsigned)p.grid), dim3(kThreads),
+           s, p, p.worklist, p.n_items);
     return hipGetLastError();
 }
 

@@ -261,7 +261,7 @@ hipError_t launch_one(const ProjLaunch& p, hipStream_t s)
     auto kernel = p.block_size < 32 ? prefill_kernel<DT, BITS, FC1, MT, ZP, true>
                                     : prefill_kernel<DT, BITS, FC1, MT, ZP, false>;
     const int64_t grid = persistent_grid(kernel, MT * 4, p.grid > 0 ? p.grid : 1);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(MT * 4), 0, s, p);
+    launch(kernel, dim3((unsigned)grid), dim3(MT * 4), s, p);
     return hipGetLastError();
 }
 

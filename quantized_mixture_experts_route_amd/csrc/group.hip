@@ -175,7 +175,7 @@ hipError_t launch_group(const int32_t* ids, int R, int E, int m_tile, int nt1, i
                         int32_t* sorted, int32_t* wl1, int64_t cap1, int32_t* n1, int nt2,
                         int32_t* wl2, int64_t cap2, int32_t* n2, hipStream_t s)
 {
-    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), 0, s, ids, R, E, m_tile, nt1,
+    launch(group_kernel, dim3(1), dim3(kThreads), s, ids, R, E, m_tile, nt1,
                        offsets, sorted, wl1, cap1, n1, nt2, wl2, cap2, n2);
     return hipGetLastError();
 }

@@ -108,10 +108,10 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(
 }
 
 template <int EPL>
-hipError_t launch(const float* logits, int T, int E, int top_k, int normalize, float* weights,
+hipError_t launch_epl(const float* logits, int T, int E, int top_k, int normalize, float* weights,
                   int32_t* ids_out, float* w_out, int32_t* tiles, int32_t* n_tiles, hipStream_t s)
 {
-    hipLaunchKernelGGL(decode_plan_kernel<EPL>, dim3(1), dim3(kThreads), 0, s, logits, T, E, top_k,
+    launch(decode_plan_kernel<EPL>, dim3(1), dim3(kThreads), s, logits, T, E, top_k,
                        normalize, weights, ids_out, w_out, tiles, n_tiles);
     return hipGetLastError();
 }
@@ -124,11 +124,11 @@ hipError_t launch_decode_plan(const float* logits, int T, int E, int top_k, int 
 {
     if (T < 1 || T * top_k > kDecodeMaxRoutes) return hipErrorInvalidValue;
     const int epl = (E + kWave - 1) / kWave;
-    if (epl <= 1) return launch<1>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
-    if (epl <= 2) return launch<2>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
-    if (epl <= 4) return launch<4>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
-    if (epl <= 8) return launch<8>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
-    return launch<16>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
+    if (epl <= 1) return launch_epl<1>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
+    if (epl <= 2) return launch_epl<2>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
+    if (epl <= 4) return launch_epl<4>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
+    if (epl <= 8) return launch_epl<8>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
+    return launch_epl<16>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
 }
 
 }  // namespace qmoe

@@ -51,6 +51,16 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // ---------------------------------------------------------------- kernel timer
+}  // namespace
+
+qmoe::LaunchEvents& qmoe::launch_events()
+{
+    static thread_local LaunchEvents ev;
+    return ev;
+}
+
+namespace {
+
 struct Timer {
     std::mutex mu;
     int stage = -1;
@@ -60,18 +70,20 @@ struct Timer {
 Timer g_timer;
 constexpr size_t kTimerPairs = 4096;
 
-void timer_begin(int stage, hipStream_t s)
+// The timed stage's next kernel records the event pair in its own dispatch
+// packet (qmoe::launch), so the pair spans the kernel alone.
+void timer_begin(int stage, hipStream_t)
 {
     if (g_timer.stage == stage && g_timer.used < g_timer.start.size()) {
-        (void)hipEventRecord(g_timer.start[g_timer.used], s);
+        qmoe::launch_events() = {g_timer.start[g_timer.used], g_timer.stop[g_timer.used]};
     }
 }
 
-void timer_end(int stage, hipStream_t s)
+void timer_end(int stage, hipStream_t)
 {
     if (g_timer.stage == stage && g_timer.used < g_timer.start.size()) {
-        (void)hipEventRecord(g_timer.stop[g_timer.used], s);
-        ++g_timer.used;
+        if (qmoe::launch_events().start == nullptr) ++g_timer.used;  // consumed by a launch
+        qmoe::launch_events() = {};
     }
 }
 

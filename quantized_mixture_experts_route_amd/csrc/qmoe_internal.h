@@ -2,10 +2,32 @@
 // (qmoe_api.cpp) and the kernel translation units.  Not installed.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace qmoe {
+
+// Kernel timer hook: when `start` is set, the next launch() records the pair
+// in its own dispatch packet (the kernel's start and end, the timestamps a
+// profiler reads) and clears it.  Thread-local; set by the C ABI's timer.
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+template <class Kernel, class... Args>
+inline void launch(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, Args... args)
+{
+    LaunchEvents& ev = launch_events();
+    if (ev.start) {
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+        ev = LaunchEvents{};
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+    }
+}
 
 // Tile shapes.  Prefill: a workgroup computes MT routed rows of one expert
 // against 4*MT weight rows (MT/16 wavefronts x 64 rows); MT is

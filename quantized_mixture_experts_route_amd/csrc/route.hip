@@ -23,11 +23,11 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 }
 
 template <int EPL>
-hipError_t launch(const float* logits, int64_t T, int E, int top_k, int normalize, int32_t* ids,
+hipError_t launch_epl(const float* logits, int64_t T, int E, int top_k, int normalize, int32_t* ids,
                   float* weights, hipStream_t s)
 {
     const int64_t blocks = (T + 3) / 4;
-    hipLaunchKernelGGL(route_kernel<EPL>, dim3((unsigned)blocks), dim3(256), 0, s, logits, T, E,
+    launch(route_kernel<EPL>, dim3((unsigned)blocks), dim3(256), s, logits, T, E,
                        top_k, normalize, ids, weights);
     return hipGetLastError();
 }
@@ -38,11 +38,11 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int top_k, int no
                         int32_t* ids, float* weights, hipStream_t s)
 {
     const int epl = (E + kWave - 1) / kWave;
-    if (epl <= 1) return launch<1>(logits, T, E, top_k, normalize, ids, weights, s);
-    if (epl <= 2) return launch<2>(logits, T, E, top_k, normalize, ids, weights, s);
-    if (epl <= 4) return launch<4>(logits, T, E, top_k, normalize, ids, weights, s);
-    if (epl <= 8) return launch<8>(logits, T, E, top_k, normalize, ids, weights, s);
-    return launch<16>(logits, T, E, top_k, normalize, ids, weights, s);
+    if (epl <= 1) return launch_epl<1>(logits, T, E, top_k, normalize, ids, weights, s);
+    if (epl <= 2) return launch_epl<2>(logits, T, E, top_k, normalize, ids, weights, s);
+    if (epl <= 4) return launch_epl<4>(logits, T, E, top_k, normalize, ids, weights, s);
+    if (epl <= 8) return launch_epl<8>(logits, T, E, top_k, normalize, ids, weights, s);
+    return launch_epl<16>(logits, T, E, top_k, normalize, ids, weights, s);
 }
 
 }  // namespace qmoe

@@ -228,6 +228,27 @@ def test_layer_decode_prefill_boundary(T, k):
     _layer_check(spec, 77 + T)
 
 
+@pytest.mark.parametrize("dtype,bits,zp,bs,act", [(2, (4, 4), "sym", 128, 0),
+                                                  (1, (4, 2), "u8", 64, 1),
+                                                  (2, (3, 2), "zpo", 32, 0)])
+def test_layer_large_prefill_tile(dtype, bits, zp, bs, act):
+    # 4096 routes against I = 8192: enough items for the 128-row prefill tile
+    spec = synth.custom(T=2048, H=256, I=8192, E=4, k=2, fc1_bits=bits[0], fc2_bits=bits[1],
+                        block_size=bs, dtype=dtype, act=act, zp_mode=zp,
+                        zpo=1.5 if zp == "zpo" else math.nan, zp_range=(0, 3),
+                        name=f"large_tile_{dtype}_{bits}_{zp}_{bs}")
+    tokens = np.unique(np.concatenate([np.linspace(0, 2047, 62).astype(np.int64), [1, 2046]]))
+    _layer_check(spec, 900 + bs, tokens=tokens)
+
+
+@pytest.mark.parametrize("T", [3, 70])
+def test_layer_block_size_16(T):
+    # 16-input blocks: each 32-code span holds two blocks (decode T=3, prefill T=70)
+    spec = synth.custom(T=T, H=256, I=256, E=6, k=2, fc1_bits=4, fc2_bits=3, block_size=16,
+                        dtype=1 + T % 2, zp_mode="u8", zp_range=(0, 7), name=f"bs16_T{T}")
+    _layer_check(spec, 60 + T)
+
+
 @pytest.mark.parametrize("T", [5, 300])
 def test_layer_all_tokens_one_expert(T):
     spec = synth.custom(T=T, H=256, I=256, E=8, k=1, fc1_bits=3, fc2_bits=4, block_size=32,
