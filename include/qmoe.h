@@ -74,8 +74,9 @@ extern "C" {
  *                24-bit word of group kk/8 [PR 33569, 24-bit 8-code INT3
  *                unpacking].  16-byte aligned.
  *   scales       fp16/bf16 (the layer's dtype) [E, N, K/block_size]; block
- *                b covers inputs [b*block_size, (b+1)*block_size).  4-byte
- *                aligned.
+ *                b covers inputs [b*block_size, (b+1)*block_size).  2-byte
+ *                aligned (16-byte alignment lets the decode kernels stage a
+ *                row's scales with 16-byte loads).
  *   zero_points  NULL, or uint8 [E, N, Z]: bits-wide values packed like the
  *                2/4-bit codes with Z = ceil((K/block_size)/(8/bits)), or one
  *                byte per block for bits = 3 (Z = K/block_size).
