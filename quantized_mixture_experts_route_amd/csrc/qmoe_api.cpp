@@ -87,6 +87,9 @@ void timer_end(int stage, hipStream_t)
     }
 }
 
+static_assert(QMOE_DECODE_MAX_ROUTES == qmoe::kDecodeRoutes, "decode switch");
+static_assert(QMOE_DECODE_MAX_ROUTES <= qmoe::kDecodeMaxRoutes, "decode plan capacity");
+
 // ---------------------------------------------------------------- workspace
 constexpr size_t kAlign = 256;
 
@@ -346,13 +349,22 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
 
-    if (L.decode) {  // routing, grouping and the m-tile list in one launch
+    // Expert-stationary decode: every (expert, column block) gets a workgroup
+    // that streams its weights before routing is known; fc1 routes by itself.
+    // Chosen when every expert is likely selected, K fits one chunk and fc1's
+    // block of weights fits the kernel's LDS staging (2-bit codes, no
+    // zero-point tensor: the other variants run out of registers).
+    const bool expert_mode = L.decode && E <= 64 && E <= R && H <= 2048 && I <= 2048 &&
+                             fc1->bits == 2 && fc1->zero_points == nullptr;
+    qmoe::DecodePlan plan{logits, (int)T, E, normalize, w, topk_ids_out, topk_w_out, offsets, sorted};
+    const qmoe::DecodePlan* dplan = expert_mode ? &plan : nullptr;
+    if (L.decode && !expert_mode) {  // routing, grouping and the m-tile list in one launch
         timer_begin(QMOE_STAGE_ROUTE, s);
         e = qmoe::launch_decode_plan(logits, (int)T, E, top_k, normalize, w, topk_ids_out,
                                      topk_w_out, wl1, n1, s);
         timer_end(QMOE_STAGE_ROUTE, s);
         if (e != hipSuccess) return hip_fail(e, "decode plan launch");
-    } else {
+    } else if (!L.decode) {
         timer_begin(QMOE_STAGE_ROUTE, s);
         e = qmoe::launch_route(logits, T, E, top_k, normalize, ids, w, s);
         timer_end(QMOE_STAGE_ROUTE, s);
@@ -381,7 +393,7 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     p1.act = activation;
     p1.act_out = act;
     timer_begin(QMOE_STAGE_FC1, s);
-    e = L.decode ? qmoe::launch_fc1_decode(p1, dtype, s) : qmoe::launch_fc1_prefill(p1, dtype, s);
+    e = L.decode ? qmoe::launch_fc1_decode(p1, dplan, dtype, s) : qmoe::launch_fc1_prefill(p1, dtype, s);
     timer_end(QMOE_STAGE_FC1, s);
     if (e != hipSuccess) return hip_fail(e, "fc1 launch");
 
@@ -400,7 +412,7 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     p2.grid = L.cap2 > 0 ? L.cap2 : 1;
     p2.y2 = y2;
     timer_begin(QMOE_STAGE_FC2, s);
-    e = L.decode ? qmoe::launch_fc2_decode(p2, dtype, s) : qmoe::launch_fc2_prefill(p2, dtype, s);
+    e = L.decode ? qmoe::launch_fc2_decode(p2, dplan, dtype, s) : qmoe::launch_fc2_prefill(p2, dtype, s);
     timer_end(QMOE_STAGE_FC2, s);
     if (e != hipSuccess) return hip_fail(e, "fc2 launch");
 

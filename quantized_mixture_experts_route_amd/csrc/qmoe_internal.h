@@ -56,6 +56,7 @@ constexpr int kDecodeTileInts = 4 + 2 * kDecodeMT;
 constexpr int kDecodeTileTokens = 4;               // first token id
 constexpr int kDecodeTileRoutes = 4 + kDecodeMT;   // first route id
 constexpr int kDecodeMaxRoutes = 128;  // routes the fused decode plan holds in LDS
+constexpr int kDecodeRoutes = 80;      // decode path for R <= this (QMOE_DECODE_MAX_ROUTES)
 
 struct ProjArgs {
     const uint8_t* codes;
@@ -85,6 +86,20 @@ struct ProjLaunch {
     float* y2;                // fc2: float32 [R, H] by route id
 };
 
+// Routing inputs and outputs of the expert-stationary decode kernels: fc1
+// routes the tokens itself and writes the plan, fc2 reads offsets/sorted.
+struct DecodePlan {
+    const float* logits;  // [T, E]
+    int T;
+    int E;
+    int normalize;
+    float* weights;       // [R] routing weights (read by the combine)
+    int32_t* ids_out;     // nullable [R]
+    float* w_out;         // nullable [R]
+    int32_t* offsets;     // [E+1] expert offsets into the sorted routes
+    int32_t* sorted;      // [R] route ids grouped by expert, ascending
+};
+
 hipError_t launch_route(const float* logits, int64_t T, int E, int top_k, int normalize,
                         int32_t* ids, float* weights, hipStream_t s);
 
@@ -100,8 +115,10 @@ hipError_t launch_decode_plan(const float* logits, int T, int E, int top_k, int 
 
 hipError_t launch_fc1_prefill(const ProjLaunch& p, int dtype, hipStream_t s);
 hipError_t launch_fc2_prefill(const ProjLaunch& p, int dtype, hipStream_t s);
-hipError_t launch_fc1_decode(const ProjLaunch& p, int dtype, hipStream_t s);
-hipError_t launch_fc2_decode(const ProjLaunch& p, int dtype, hipStream_t s);
+// plan == nullptr: the m-tile list path (p.worklist / p.n_items); otherwise
+// the expert-stationary kernels (K <= 2048, E <= 64, R <= kDecodeMaxRoutes).
+hipError_t launch_fc1_decode(const ProjLaunch& p, const DecodePlan* plan, int dtype, hipStream_t s);
+hipError_t launch_fc2_decode(const ProjLaunch& p, const DecodePlan* plan, int dtype, hipStream_t s);
 
 hipError_t launch_combine(const float* y2, const float* weights, int64_t T, int H, int top_k,
                           void* out, int dtype, hipStream_t s);

@@ -30,10 +30,11 @@ __device__ inline float key_to_logit(int32_t key)
     return __builtin_bit_cast(float, key < 0 ? (key ^ 0x7fffffff) : key);
 }
 
-// Routes the token whose E logits start at `row`; the whole wavefront calls
-// it.  For every slot s < top_k exactly one lane calls emit(s, expert, weight).
-template <int EPL, class Emit>
-__device__ inline void route_token(const float* row, int E, int top_k, int normalize, Emit emit)
+// Routes one token; the whole wavefront calls it.  get(j) returns this lane's
+// logit of expert lane + 64 j (called only for experts < E).  For every slot
+// s < top_k exactly one lane calls emit(s, expert, weight).
+template <int EPL, class Get, class Emit>
+__device__ inline void route_values(int E, int top_k, int normalize, Get get, Emit emit)
 {
     const int lane = threadIdx.x & (kWave - 1);
     uint64_t cand[EPL];
@@ -43,7 +44,7 @@ __device__ inline void route_token(const float* row, int E, int top_k, int norma
         const int e = lane + kWave * j;
         cand[j] = 0;
         if (e < E) {
-            const float v = row[e];
+            const float v = get(j);
             const uint32_t ukey = (uint32_t)route_key(v) ^ 0x80000000u;
             cand[j] = ((uint64_t)ukey << 32) | (uint32_t)~(uint32_t)e;
             if (v > m) {
@@ -86,7 +87,7 @@ __device__ inline void route_token(const float* row, int E, int top_k, int norma
         for (int j = 0; j < EPL; ++j) {
             const int e = lane + kWave * j;
             if (e < E) {
-                part += expf(row[e] - m);
+                part += expf(get(j) - m);
             }
         }
         den = wave_sum_f32(part);
@@ -98,6 +99,14 @@ __device__ inline void route_token(const float* row, int E, int top_k, int norma
             emit(s, my_id[j], my_num[j] / den);
         }
     }
+}
+
+// Routes the token whose E logits start at `row`.
+template <int EPL, class Emit>
+__device__ inline void route_token(const float* row, int E, int top_k, int normalize, Emit emit)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    route_values<EPL>(E, top_k, normalize, [&](int j) { return row[lane + kWave * j]; }, emit);
 }
 
 }  // namespace qmoe

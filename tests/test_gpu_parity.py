@@ -249,6 +249,22 @@ def test_layer_block_size_16(T):
     _layer_check(spec, 60 + T)
 
 
+@pytest.mark.parametrize("T,k,E,skew", [(40, 2, 2, False), (33, 2, 4, False), (40, 1, 4, True),
+                                        (12, 3, 8, False), (80, 1, 64, False)])
+def test_layer_decode_expert_stationary(T, k, E, skew):
+    # E <= R decode: one workgroup per (expert, column block), fc1 routes the
+    # tokens itself; experts with more than 16 routes take several m-tiles,
+    # experts with none exit (skew sends every token to expert 0)
+    spec = synth.custom(T=T, H=256, I=384, E=E, k=k, fc1_bits=2, fc2_bits=4, block_size=128,
+                        dtype=1 + T % 2, act=T % 2, zp_mode="zpo", zpo=1.5,
+                        name=f"expert_stationary_T{T}_k{k}_E{E}")
+    logits = None
+    if skew:
+        logits = np.zeros((T, E), dtype=np.float32)
+        logits[:, 0] = 3.0
+    _layer_check(spec, 40 + T + E, logits=logits)
+
+
 @pytest.mark.parametrize("T", [5, 300])
 def test_layer_all_tokens_one_expert(T):
     spec = synth.custom(T=T, H=256, I=256, E=8, k=1, fc1_bits=3, fc2_bits=4, block_size=32,
