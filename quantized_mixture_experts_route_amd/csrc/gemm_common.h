@@ -92,7 +92,7 @@ template <int DT, int BITS, int ZP>
 __device__ inline u32x4 dequant_zp(const Span<BITS>& sp, int t, const BlockParams& b)
 {
     if constexpr (ZP == kZpGeneric) return dequant_step_generic<DT, BITS>(sp, t, b.zp, b.scale);
-    else return dequant_step<DT, BITS>(sp, t, b.zp, b.scale);
+    else return dequant_step<DT, BITS, ZP == kZpTensor>(sp, t, b.zp, b.scale);
 }
 
 inline int zp_mode(const ProjArgs& w)

@@ -118,14 +118,17 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
         }
         __syncthreads();
 
-        // this thread's A span: row tid/4, inputs [32*(tid%4), +32) of a super-step
-        const uint16_t* a_ptr = a_src + (int64_t)row_src[tid >> 2] * K + 32 * (tid & 3);
+        // this thread's A span: inputs [32*a_sp, +32) of a super-step of tile
+        // row a_r (four consecutive lanes read one row's 256 contiguous bytes)
+        const int a_r = tid >> 2;
+        const int a_sp = tid & 3;
+        const uint16_t* a_ptr = a_src + (int64_t)row_src[a_r] * K + 32 * a_sp;
         uint32_t a_stage[16];
         auto load_a = [&](int s) { load_a_span(a_ptr, s * kSuperK, a_stage); };
         auto store_a = [&](uint32_t* buf) {
             uint32_t perm[16];
             permute_span<O>(a_stage, perm);
-            uint32_t* dst = buf + (tid >> 2) * kPitch + 16 * (tid & 3);
+            uint32_t* dst = buf + a_r * kPitch + 16 * a_sp;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 *reinterpret_cast<u32x4*>(dst + 4 * v) =

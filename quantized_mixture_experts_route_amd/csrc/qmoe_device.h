@@ -226,12 +226,13 @@ __host__ __device__ inline bool zp_is_half_integer(float zp)
 // [PR 33569: dequantized weights are rounded to the activation type before
 // accumulation].
 //
-// Both dtypes first place each code at mantissa bits 1.. of the fp16 value
-// 0x6000 (512.0, spacing 0.5), so the register reads as the fp16 pair
-// (512 + code, 512 + code').
-// fp16: subtracting 512 + zp is exact for half-integer zp, and the packed
-// multiply by the fp16 scale rounds once.
-// bf16: v_fma_mix_f32 forms (512 + code)*s - (512 + zp)*s from the fp16
+// Both dtypes first place each code in the mantissa of an fp16 value: at
+// bits 1.. of 0x6000 (512.0, spacing 0.5), so the register reads as the fp16
+// pair (512 + code, 512 + code'); int4 with bf16 or an integer zero point
+// uses two bases instead (1024 + code at bits 0..3, 64 + code at bits 4..7).
+// fp16: subtracting base + zp is exact, and the packed multiply by the fp16
+// scale rounds once.
+// bf16: v_fma_mix_f32 forms (base + code)*s - (base + zp)*s from the fp16
 // halves; both terms are exact in float32 (at most 11 + 8 significant bits),
 // so the result is (code - zp)*s exactly and v_cvt_pk_bf16_f32 rounds once.
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -258,53 +259,75 @@ __device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic)
     return (x & opaque_s(mask)) | magic;
 }
 
-template <int DT, int BITS>
+// INTZP: the zero point is known to be an integer (a uint8 tensor), which
+// lets fp16 use the two-base int4 unpacking below too.
+template <int DT, int BITS, bool INTZP = false>
 __device__ inline u32x4 dequant_step(const Span<BITS>& sp, int t, float zp, float scale)
 {
-    // codes to fp16 (512 + q): one v_and_or per register (two codes)
-    const uint32_t kMagic = opaque(0x60006000u);
+    // int4 with two bases: codes of nibbles 0/4 and 2/6 sit at mantissa bits
+    // 0..3 of 1024.0 (spacing 1), nibbles 1/5 and 3/7 at bits 4..7 of 64.0
+    // (spacing 1/16), so one shift serves four registers.  Exact for any
+    // zero point in bf16 (applied in float32) and for integer ones in fp16.
+    constexpr bool kTwoBase = BITS == 4 && (DT == kBF16 || INTZP);
     uint32_t raw[4];
-    if constexpr (BITS == 4) {
+    float base[2];  // base of even and odd registers
+    if constexpr (kTwoBase) {
+        const uint32_t lo = opaque(0x64006400u), hi = opaque(0x54005400u);
         const uint32_t g = sp.w[t];
-        raw[0] = and_or(g << 1, 0x001e001eu, kMagic);
-#pragma unroll
-        for (int r = 1; r < 4; ++r) raw[r] = and_or(g >> (4 * r - 1), 0x001e001eu, kMagic);
-    } else if constexpr (BITS == 2) {
-        const uint32_t w = sp.w[t >> 1];
-        const int j0 = 4 * (t & 1);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = j0 + r;
-            raw[r] = and_or(j == 0 ? (w << 1) : (w >> (2 * j - 1)), 0x00060006u, kMagic);
-        }
+        const uint32_t h = g >> 8;
+        raw[0] = and_or(g, 0x000f000fu, lo);  // codes 0, 4
+        raw[1] = and_or(g, 0x00f000f0u, hi);  // codes 1, 5
+        raw[2] = and_or(h, 0x000f000fu, lo);  // codes 2, 6
+        raw[3] = and_or(h, 0x00f000f0u, hi);  // codes 3, 7
+        base[0] = 1024.0f;
+        base[1] = 64.0f;
     } else {
-        const uint32_t g = span_group<3>(sp, t);
-        const uint32_t y = (g & 0xfffu) | ((g << 4) & 0x0fff0000u);  // codes 4-7 to bit 16
-        raw[0] = and_or(y << 1, 0x000e000eu, kMagic);
+        // codes to fp16 (512 + q): one v_and_or per register (two codes)
+        const uint32_t kMagic = opaque(0x60006000u);
+        base[0] = base[1] = 512.0f;
+        if constexpr (BITS == 4) {
+            const uint32_t g = sp.w[t];
+            raw[0] = and_or(g << 1, 0x001e001eu, kMagic);
 #pragma unroll
-        for (int r = 1; r < 4; ++r) raw[r] = and_or(y >> (3 * r - 1), 0x000e000eu, kMagic);
+            for (int r = 1; r < 4; ++r) raw[r] = and_or(g >> (4 * r - 1), 0x001e001eu, kMagic);
+        } else if constexpr (BITS == 2) {
+            const uint32_t w = sp.w[t >> 1];
+            const int j0 = 4 * (t & 1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = j0 + r;
+                raw[r] = and_or(j == 0 ? (w << 1) : (w >> (2 * j - 1)), 0x00060006u, kMagic);
+            }
+        } else {
+            const uint32_t g = span_group<3>(sp, t);
+            const uint32_t y = (g & 0xfffu) | ((g << 4) & 0x0fff0000u);  // codes 4-7 to bit 16
+            raw[0] = and_or(y << 1, 0x000e000eu, kMagic);
+#pragma unroll
+            for (int r = 1; r < 4; ++r) raw[r] = and_or(y >> (3 * r - 1), 0x000e000eu, kMagic);
+        }
     }
     u32x4 out;
     if constexpr (DT == kF16) {
-        // (512 + q) - (512 + zp) is exact in fp16 for half-integer zp; one
-        // rounding in the multiply
-        const _Float16 c = (_Float16)(-(512.0f + zp));
-        const f16x2 c2 = {c, c};
+        // (base + q) - (base + zp) is exact in fp16 (half-integer zp at base
+        // 512, integer zp at 1024 and 64); one rounding in the multiply
         const _Float16 sh = (_Float16)scale;
         const f16x2 s2 = {sh, sh};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+            const _Float16 c = (_Float16)(-(base[r & 1] + zp));
+            const f16x2 c2 = {c, c};
             const f16x2 v = (__builtin_bit_cast(f16x2, raw[r]) + c2) * s2;
             out[r] = __builtin_bit_cast(uint32_t, v);
         }
     } else {
-        // (512 + q) * s - (512 + zp) * s in one fused multiply-add with fp16
+        // (base + q)*s - (base + zp)*s in one fused multiply-add with fp16
         // inputs (v_fma_mix_f32): both products are exact in float32, so the
-        // result is (q - zp) * s exactly, rounded once to bf16
-        const float c = -(512.0f + zp) * scale;
+        // result is (q - zp)*s exactly, rounded once to bf16
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const float c0 = -(base[0] + zp) * scale, c1 = -(base[1] + zp) * scale;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+            const float c = (r & 1) ? c1 : c0;
             const f16x2 h = __builtin_bit_cast(f16x2, raw[r]);
             const bf16x2 v = {(__bf16)__builtin_fmaf((float)h.x, scale, c),
                               (__bf16)__builtin_fmaf((float)h.y, scale, c)};
