@@ -162,7 +162,9 @@ size_t qmoe_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t t
  *   workspace   >= qmoe_workspace_size(T, H, I, E, top_k, dtype) bytes,
  *               256-byte aligned; contents on entry do not matter.
  * Requires 1 <= E <= 1024, 1 <= top_k <= E, H and I multiples of 128,
- * bits in {2,3,4} per projection.  T = 0 returns QMOE_OK and enqueues nothing.
+ * bits in {2,3,4} per projection, T*H < 2^32 and T*top_k*I < 2^32 (the
+ * projection kernels address their inputs with 32-bit element offsets).
+ * T = 0 returns QMOE_OK and enqueues nothing.
  * Numerics: dequantized weights are rounded to dtype (round to nearest even)
  * before the products, products accumulate in float32, the activation is
  * rounded to dtype, fc2 outputs stay float32 until the combine.

@@ -3,10 +3,9 @@
 // A workgroup of MT/16 wavefronts takes one work-list item: up to MT routed
 // rows of one expert against 4*MT weight rows, each wavefront owning 64
 // weight rows (4 MFMA column blocks of 16) for all MT rows, so each weight
-// element is dequantized once per MT rows.  Every thread stages exactly one
-// 32-value A span per K super-step, and a wavefront keeps within 256
-// registers, so two wavefronts share each SIMD and one hides the other's
-// waits.  MT = 128 (8 wavefronts, 512 weight rows, one workgroup per CU) for
+// element is dequantized once per MT rows.  Every thread stages four 16-byte
+// A chunks per K super-step, and a wavefront keeps within 256 registers, so
+// two wavefronts share each SIMD and one hides the other's waits.  MT = 128 (8 wavefronts, 512 weight rows, one workgroup per CU) for
 // large layers; MT = 64 (4 wavefronts, 256 weight rows, two per CU) when the
 // large tile leaves too few items, and for 16-input blocks and generic zero
 // points, whose extra registers only fit the small tile.
@@ -49,7 +48,7 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
 {
     constexpr Order O = code_order<DT, BITS>();
     constexpr int MB = MT / 16;
-    constexpr int kThreads = MT * 4;        // one (row, lane-group span) per thread
+    constexpr int kThreads = MT * 4;        // 16 tile rows staged per wavefront
     constexpr int kRows = MT * 4;           // weight rows per item (64 per wavefront)
     __shared__ __attribute__((aligned(16))) uint32_t a_lds[2][MT * kPitch];
     __shared__ int row_src[MT];  // A row of tile row i
@@ -118,21 +117,31 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
         }
         __syncthreads();
 
-        // this thread's A span: inputs [32*a_sp, +32) of a super-step of tile
-        // row a_r (four consecutive lanes read one row's 256 contiguous bytes)
-        const int a_r = tid >> 2;
-        const int a_sp = tid & 3;
-        const uint16_t* a_ptr = a_src + (int64_t)row_src[a_r] * K + 32 * a_sp;
-        uint32_t a_stage[16];
-        auto load_a = [&](int s) { load_a_span(a_ptr, s * kSuperK, a_stage); };
-        auto store_a = [&](uint32_t* buf) {
-            uint32_t perm[16];
-            permute_span<O>(a_stage, perm);
-            uint32_t* dst = buf + a_r * kPitch + 16 * a_sp;
+        // A staging: wavefront w stages tile rows [16w, 16w+16) of each
+        // super-step.  Load q of a thread reads the 16-byte chunk (lane & 15)
+        // of row 16w + 4q + (lane >> 4), so each instruction covers four rows
+        // with whole 128-byte lines; the chunk is permuted to its MFMA step on
+        // the way to LDS (int2's order pairs neighbouring chunks, exchanged
+        // between lanes l and l^1).
+        const int a_j = lane & 15;
+        const int a_r0 = 16 * wave + (lane >> 4);
+        uint32_t a_off[4];  // element offsets (the host keeps A below 2^32 elements)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                *reinterpret_cast<u32x4*>(dst + 4 * v) =
-                    u32x4{perm[4 * v], perm[4 * v + 1], perm[4 * v + 2], perm[4 * v + 3]};
+        for (int q = 0; q < 4; ++q) a_off[q] = (uint32_t)row_src[a_r0 + 4 * q] * (uint32_t)K + 8 * a_j;
+        u32x4 a_stage[4];
+        auto load_a = [&](int s) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a_stage[q] = *reinterpret_cast<const u32x4*>(a_src + (a_off[q] + (uint32_t)(s * kSuperK)));
+            }
+        };
+        auto store_a = [&](uint32_t* buf) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u32x4 v;
+                if constexpr (O == Order::kStride8) v = permute_chunk_pair(a_stage[q], lane & 1);
+                else v = permute_chunk<O>(a_stage[q]);
+                *reinterpret_cast<u32x4*>(buf + (a_r0 + 4 * q) * kPitch + 4 * a_j) = v;
             }
         };
         // scale and zero-point byte of the block holding input kk of row nb

@@ -128,6 +128,8 @@ bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L,
     if (!mul_ok(R, (int64_t)I * 2, &act_bytes) || !mul_ok(R, (int64_t)H * 4, &y2_bytes)) {
         return false;
     }
+    // the projection kernels address hidden [T, H] and act [R, I] with 32-bit element offsets
+    if (T * (int64_t)H >= (int64_t(1) << 32) || R * (int64_t)I >= (int64_t(1) << 32)) return false;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;

@@ -211,6 +211,50 @@ __device__ inline void permute_span(const uint32_t (&in)[16], uint32_t (&out)[16
     }
 }
 
+// Chunk j of a super-step row (its 8 values 8j..8j+7, value 2i in the low
+// half of in[i]) -> the A registers of MFMA step j % 4 of span j / 4, for the
+// orders whose step reads one chunk (kNatural, kStride4).
+template <Order O>
+__device__ inline u32x4 permute_chunk(const u32x4& in)
+{
+    static_assert(O != Order::kStride8, "kStride8 steps read two chunks: use permute_chunk_pair");
+    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int lo = order_lo(O, 0, r), hi = order_hi(O, 0, r);
+        if constexpr (O == Order::kNatural) {
+            out[r] = w[r];
+        } else {
+            const uint32_t sel = ((lo & 1) ? 0x0302u : 0x0100u) |
+                                 ((hi & 1) ? 0x07060000u : 0x05040000u);
+            out[r] = __builtin_amdgcn_perm(w[hi >> 1], w[lo >> 1], sel);
+        }
+    }
+    return u32x4{out[0], out[1], out[2], out[3]};
+}
+
+// kStride8: step 2m + u of a span reads values 4u..4u+3 of chunks 2m and
+// 2m+1 (register r pairs value 4u+r of the first with value 4u+r of the
+// second).  Lanes l and l^1 hold chunks 2m (even lane) and 2m+1 (odd lane) of
+// one row; each keeps the half of its chunk that its own step reads, sends
+// the other half to its neighbour, and returns the registers of step
+// (its chunk) % 4.
+__device__ inline u32x4 permute_chunk_pair(const u32x4& in, bool odd)
+{
+    const uint32_t send0 = odd ? in.x : in.z, send1 = odd ? in.y : in.w;
+    const uint32_t keep0 = odd ? in.z : in.x, keep1 = odd ? in.w : in.y;
+    constexpr int kSwapPairs = 0xb1;  // DPP quad_perm [1,0,3,2]
+    const uint32_t recv0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send0, kSwapPairs, 0xf, 0xf, false);
+    const uint32_t recv1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send1, kSwapPairs, 0xf, 0xf, false);
+    // v_perm_b32(a, b, sel): bytes 0-3 of b, 4-7 of a.  The even chunk's value
+    // goes to the low half: the even lane's own (b), the odd lane's received (a).
+    const uint32_t sel_lo = odd ? 0x01000504u : 0x05040100u;  // low 16 bits of both words
+    const uint32_t sel_hi = odd ? 0x03020706u : 0x07060302u;  // high 16 bits of both words
+    return u32x4{__builtin_amdgcn_perm(recv0, keep0, sel_lo), __builtin_amdgcn_perm(recv0, keep0, sel_hi),
+                 __builtin_amdgcn_perm(recv1, keep1, sel_lo), __builtin_amdgcn_perm(recv1, keep1, sel_hi)};
+}
+
 // ---------------------------------------------------------------- dequant
 // Zero points that are multiples of 1/2 and below 256 in magnitude (integer
 // tensors, symmetric centres, the 1.5 offset of the int2 worked example) take

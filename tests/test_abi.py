@@ -66,6 +66,10 @@ def test_workspace_size_monotone_and_invalid():
     assert qm.workspace_size(8, 2048, 2048, 8, 2, 3) == 0
     assert qm.workspace_size(8, 0, 2048, 8, 2, 1) == 0
     assert qm.workspace_size(1 << 40, 2048, 2048, 8, 2, 1) == 0
+    # inputs are addressed with 32-bit element offsets: T*H and T*top_k*I stay below 2^32
+    assert qm.workspace_size((1 << 20) - 1, 4096, 1024, 8, 2, 1) > 0
+    assert qm.workspace_size(1 << 20, 4096, 1024, 8, 2, 1) == 0
+    assert qm.workspace_size(1 << 19, 1024, 4096, 8, 2, 1) == 0
 
 
 def _proj(bits=4, codes=FAKE, scales=FAKE, zp=None):
