@@ -43,7 +43,11 @@ constexpr int kXcds = 8;
 
 // TWO: block_size 16, so the two halves of a 32-code span have their own
 // scale and zero point.
-template <int DT, int BITS, bool FC1, int MT, int ZP, bool TWO>
+// STAGED: each wavefront copies the scales of its 64 weight rows into LDS
+// eight blocks at a time (one 16-byte load per lane, a row per lane, issued a
+// stage ahead), and reads each super-step's scales from there; without it
+// every super-step loads them from HBM, 16 rows per instruction.
+template <int DT, int BITS, bool FC1, int MT, int ZP, bool TWO, bool STAGED>
 __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
 {
     constexpr Order O = code_order<DT, BITS>();
@@ -53,6 +57,8 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
     __shared__ __attribute__((aligned(16))) uint32_t a_lds[2][MT * kPitch];
     __shared__ int row_src[MT];  // A row of tile row i
     __shared__ int row_dst[MT];  // fc2: y2 row (route id) of tile row i
+    // STAGED: per wavefront, 64 row slots of 8 scales
+    __shared__ __attribute__((aligned(16))) uint16_t sc_lds[STAGED ? MT / 16 : 1][STAGED ? 64 * 8 : 1];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -107,6 +113,18 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
         const uint16_t* scales_e = reinterpret_cast<const uint16_t*>(p.w.scales) + erow * n_blocks;
         const uint8_t* zp_e = ZP == kZpTensor ? p.w.zp + erow * zp_bytes : nullptr;
 
+        // STAGED: lane l loads row l of the wavefront's 64 contiguous weight
+        // rows (fc1: 2*col0.., fc2: col0..) into slot l; fc1 slots are
+        // interleaved so that the rows a load of column block nb reads sit in
+        // 16 consecutive slots (no LDS bank conflicts).
+        const uint32_t wr_base = active ? (FC1 ? 2 * col0 : col0) : 0;
+        const uint16_t* sc_row = scales_e + (wr_base + lane) * n_blocks;
+        const int sc_slot_store = FC1 ? ((lane >> 1) | ((lane & 1) << 5)) : lane;
+        const int ss_shift = bs_shift - 4;  // super-steps per stage: block_size / 16
+        const int n_stages = (int)(n_blocks >> 3);
+        u32x4 sc_next;
+        auto stage_load = [&](int stage) { sc_next = *reinterpret_cast<const u32x4*>(sc_row + 8 * stage); };
+
         __syncthreads();  // the previous item is done with row_src and a_lds
         for (int i = tid; i < MT; i += kThreads) {
             // rows past the tile repeat its first row: their outputs are never stored
@@ -148,7 +166,12 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
         auto params = [&](int nb, int kk) {
             RawParams q;
             q.blk = kk >> bs_shift;
-            q.scale = scales_e[wrow[nb] * n_blocks + q.blk];
+            if constexpr (STAGED) {
+                constexpr int kSlot[4] = {0, FC1 ? 32 : 16, FC1 ? 16 : 32, 48};
+                q.scale = sc_lds[wave][(c + kSlot[nb]) * 8 + (q.blk & 7)];
+            } else {
+                q.scale = scales_e[wrow[nb] * n_blocks + q.blk];
+            }
             q.zp = 0;
             if constexpr (ZP == kZpTensor) {
                 q.zp = zp_e[wrow[nb] * zp_bytes + (BITS == 3 ? q.blk : q.blk >> (BITS == 2 ? 2 : 1))];
@@ -157,6 +180,13 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
         };
         auto load_b = [&](int s, Span<BITS> (&sp)[4], RawParams (&bp)[4]) {
             const int kk = s * kSuperK + 32 * g;
+            if constexpr (STAGED) {
+                if ((s & ((1 << ss_shift) - 1)) == 0) {  // first super-step of a stage
+                    *reinterpret_cast<u32x4*>(&sc_lds[wave][sc_slot_store * 8]) = sc_next;
+                    const int next = (s >> ss_shift) + 1;
+                    if (next < n_stages) stage_load(next);
+                }
+            }
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
                 sp[nb] = load_span<BITS>(codes_e + wrow[nb] * row_bytes, kk);
@@ -196,6 +226,7 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
 
         Span<BITS> sp[4];
         RawParams bp[4];
+        if constexpr (STAGED) stage_load(0);
         load_a(0);
         load_b(0, sp, bp);
         for (int s = 0; s < n_super; ++s) {
@@ -267,23 +298,44 @@ int64_t persistent_grid(Kernel kernel, int threads, int64_t item_bound)
     return (g + kXcds - 1) / kXcds * kXcds;
 }
 
-template <bool FC1, int DT, int BITS, int MT, int ZP>
-hipError_t launch_one(const ProjLaunch& p, hipStream_t s)
+// Scales can be staged eight blocks at a time when a row holds whole stages
+// and the 16-byte loads are aligned.
+inline bool can_stage(const ProjLaunch& p)
 {
-    auto kernel = p.block_size < 32 ? prefill_kernel<DT, BITS, FC1, MT, ZP, true>
-                                    : prefill_kernel<DT, BITS, FC1, MT, ZP, false>;
-    const int64_t grid = persistent_grid(kernel, MT * 4, p.grid > 0 ? p.grid : 1);
-    launch(kernel, dim3((unsigned)grid), dim3(MT * 4), s, p);
+    return p.block_size >= 32 && (p.K / p.block_size) % 8 == 0 &&
+           reinterpret_cast<uintptr_t>(p.w.scales) % 16 == 0;
+}
+
+template <class Kernel>
+hipError_t run(Kernel kernel, const ProjLaunch& p, int threads, hipStream_t s)
+{
+    const int64_t grid = persistent_grid(kernel, threads, p.grid > 0 ? p.grid : 1);
+    launch(kernel, dim3((unsigned)grid), dim3(threads), s, p);
     return hipGetLastError();
 }
 
+template <bool FC1, int DT, int BITS, int MT, int ZP>
+hipError_t launch_one(const ProjLaunch& p, hipStream_t s)
+{
+    if (can_stage(p)) return run(prefill_kernel<DT, BITS, FC1, MT, ZP, false, true>, p, MT * 4, s);
+    if constexpr (MT == kPrefillMTSmall) {
+        if (p.block_size < 32) return run(prefill_kernel<DT, BITS, FC1, MT, ZP, true, false>, p, MT * 4, s);
+        return run(prefill_kernel<DT, BITS, FC1, MT, ZP, false, false>, p, MT * 4, s);
+    }
+    return hipErrorInvalidValue;  // the large tile always stages its scales
+}
+
+// The large tile serves the fast zero-point modes with stageable scales only
+// (the host picks the small tile otherwise).
 template <bool FC1, int DT, int BITS, int MT>
 hipError_t launch_zp(const ProjLaunch& p, hipStream_t s)
 {
     switch (zp_mode(p.w)) {
     case kZpConst: return launch_one<FC1, DT, BITS, MT, kZpConst>(p, s);
     case kZpTensor: return launch_one<FC1, DT, BITS, MT, kZpTensor>(p, s);
-    default: return launch_one<FC1, DT, BITS, MT, kZpGeneric>(p, s);
+    default:
+        if constexpr (MT == kPrefillMTSmall) return launch_one<FC1, DT, BITS, MT, kZpGeneric>(p, s);
+        return hipErrorInvalidValue;
     }
 }
 

@@ -315,10 +315,13 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     if (!make_layout(T, H, I, E, top_k, &L)) return fail(QMOE_ERR_INVALID_ARG, "sizes overflow");
     if (T == 0) return ok();
     // the large prefill tile when its registers fit (block_size >= 32, fast
-    // zero points) and it still yields a few items per CU
+    // zero points, scales staged through LDS: whole 8-block stages per row and
+    // 16-byte aligned) and it still yields a few items per CU
     const qmoe::ProjArgs w1 = proj_args(fc1, zero_point_offset);
     const qmoe::ProjArgs w2 = proj_args(fc2, zero_point_offset);
-    if (!L.decode && block_size >= 32 && w1.fast && w2.fast &&
+    const bool stageable = (H / block_size) % 8 == 0 && (I / block_size) % 8 == 0 &&
+                           aligned(w1.scales, 16) && aligned(w2.scales, 16);
+    if (!L.decode && block_size >= 32 && w1.fast && w2.fast && stageable &&
         (T * top_k / qmoe::kPrefillMTLarge) * ceil_div(I, qmoe::prefill_fc1_cols(qmoe::kPrefillMTLarge)) >= 1024) {
         make_layout(T, H, I, E, top_k, &L, qmoe::kPrefillMTLarge);
     }
