@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libqmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["qmoe_api.cpp", "route.hip", "group.hip", "plan.hip", "gemm_prefill.hip", "gemm_decode.hip",
+SOURCES = ["qmoe_api.cpp", "route.hip", "group.hip", "plan.hip", "gemm_prefill.hip", "gemm_decode.hip", "gemm_stream.hip",
            "combine.hip", "dequant.hip"]
 
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

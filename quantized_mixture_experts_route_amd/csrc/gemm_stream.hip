@@ -1,0 +1,524 @@
+// gemm_stream.hip -- decode projections that request every expert's packed
+// weights at launch and consume them as they land.
+//
+// [PR 33569: the decode path serves small expanded-row counts, and its time
+// is set by the packed-weight bytes; qmoe.rs QMoEKernel::execute: route,
+// group, fc1 + activation, fc2, combine.]  With R = T*top_k <= 16 every
+// selected expert's weights are read once and multiplied with at most 16
+// rows, so a projection costs the time to stream its bytes plus the work left
+// once the last of them arrives.  One workgroup of eight wavefronts per
+// (expert, block of weight rows); wavefront w owns one block of 16 contiguous
+// weight rows and a 1/KS share of K.  fc1 (KS = 1): 128 rows per workgroup,
+// the 16 rows of a wavefront are 8 gate/up pairs, gate in MFMA columns 0-7
+// and up in 8-15, paired in the epilogue by a DPP rotate, so nothing is
+// reduced across wavefronts.  fc2 (KS = 2 when K allows): 64 rows per
+// workgroup and two wavefronts per block, whose partial sums meet once in LDS.
+//
+// Issue order (vmcnt retires loads in issue order, so each wait covers the
+// loads it needs and no later ones; scheduling barriers keep the groups in
+// place, and a workgroup barrier puts every early load of the CU ahead of
+// every weight load, since an L2 hit queued behind misses waits for them): fc1 the router logits of the wavefront's tokens, fc2 the expert's
+// offsets and route ids; the scale table of the workgroup's rows; one A row
+// per wavefront (fc1 the tokens, all of them, since routing is not known yet;
+// fc2 the expert's rows); then every packed weight byte of the wavefront, in
+// P pieces of one 128-byte line per row, eight whole lines per load
+// instruction.  fc1 routes while the weights are in flight, and the first
+// workgroup writes the routing weights, expert offsets and sorted routes for
+// fc2 and the combine.  Piece j is consumed as soon as it lands: copied to a
+// wavefront-private LDS slot, read back as MFMA spans, and multiplied with the
+// A fragments of its super-steps, whose MFMA chains are interleaved so that
+// one wavefront keeps the matrix core busy.
+//
+// MFMA mapping and dequantization are those of the other projection kernels:
+// lane 16g + c feeds A row c (a routed row; zeros past the expert's rows,
+// without reading LDS) and weight column c of the block, lane group g the inputs
+// [32g, 32g+32) of each 128-input super-step in the code order of the dequant
+// routines.  RAW (block_size a multiple of 128): the B registers are the raw
+// codes made exact dtype values by one v_and_or_b32 each, with a base b_r per
+// register r chosen so that the code's bits, where they already sit in the
+// packed word (or nearly), weigh 1 (fp16 int2: 1024, 256, 64, 16; int4: 1024
+// and 64), which saves most of the shifts that would bring every code down to
+// bit 0.  The zero point and the bases are taken out per
+// super-step in float32: sum_k (q_k - zp) a_k = mfma(a, b_r + q) -
+// sum_k (b_r(k) + zp) a_k, the last sum formed once per A row and super-step
+// while A is staged; the scale multiplies the difference.  Otherwise each
+// weight is dequantized in registers with a constant zero point.
+#include "gemm_common.h"
+#include "route_common.h"
+
+namespace qmoe {
+namespace {
+
+constexpr int kWavesS = 8;
+constexpr int kThreadsS = kWavesS * kWave;
+constexpr int kRowsA = 16;                   // A tile rows: tokens (fc1) or expert rows (fc2)
+constexpr int kMaxK = 2048;
+constexpr int kMaxSuper = kMaxK / kSuperK;
+constexpr int kPitchA = kMaxK / 2 + 4;       // A tile row pitch in 32-bit words (row r: bank 4r)
+constexpr int kLine = 128;                   // bytes of each weight row per piece
+constexpr int kSlotPitch = kLine + 16;       // LDS slot row pitch: 36 words, 16 rows on distinct banks
+constexpr int kMaxBlocks = 64;               // quantization blocks per row (K / block_size)
+constexpr int kScPitch = kMaxBlocks + 4;     // scale table row pitch in uint16 (rows 8-byte aligned)
+constexpr int kScUnits = 2;                  // 16-byte scale units per thread at most (128 rows x 8)
+constexpr int kTokW = kRowsA / kWavesS;      // tokens each wavefront routes (T <= 16)
+constexpr int kDppRor8 = 0x128;              // DPP row_ror:8: lane c reads lane c ^ 8 of its row
+
+// A kernel argument held in SGPRs from here on: the compiler may otherwise
+// fetch it again where it is used, and a fetch issued after the weight
+// loads waits behind them.
+template <class T>
+__device__ inline T held(T v)
+{
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
+// RAW bases: register r of an MFMA step takes its code pair from the packed
+// word shifted right by raw_shift(r), at bits raw_pos(r) and raw_pos(r) + 16:
+// int2 pairs sit 2r bits up (8 more on odd steps, taken out first), int4
+// pairs 4(r & 1) bits up (8 more for r >= 2).  Fields must stay inside the
+// mantissa (10 bits fp16, 7 bits bf16), so bf16 moves int2's fourth pair and
+// int4's odd pairs down first.  The base is the power of two whose mantissa
+// gives bit raw_pos(r) weight 1: 2^(m - raw_pos(r)).
+template <int DT, int BITS>
+__host__ __device__ constexpr int raw_shift(int r)
+{
+    if (BITS == 2) return (DT == kF16 || r < 3) ? 0 : 2;
+    return (r < 2 ? 0 : 8) + ((DT == kBF16 && (r & 1)) ? 1 : 0);
+}
+
+template <int DT, int BITS>
+__host__ __device__ constexpr int raw_pos(int r)
+{
+    if (BITS == 2) return (DT == kF16 || r < 3) ? 2 * r : 4;
+    return (r & 1) ? (DT == kF16 ? 4 : 3) : 0;
+}
+
+template <int DT, int BITS>
+__host__ __device__ constexpr float raw_base(int r)
+{
+    return (float)(1 << ((DT == kF16 ? 10 : 7) - raw_pos<DT, BITS>(r)));
+}
+
+template <int DT, int BITS>
+__host__ __device__ constexpr uint32_t raw_magic(int r)
+{
+    // the dtype's bit pattern of raw_base(r), in both halves
+    constexpr int kBias = DT == kF16 ? 15 : 127;
+    constexpr int kMant = DT == kF16 ? 10 : 7;
+    const uint32_t h = (uint32_t)(kBias + kMant - raw_pos<DT, BITS>(r)) << kMant;
+    return h | (h << 16);
+}
+
+template <int DT, int BITS>
+__device__ inline u32x4 raw_step_based(const Span<BITS>& sp, int t, const uint32_t (&magic)[4])
+{
+    constexpr uint32_t kField = BITS == 2 ? 0x00030003u : 0x000f000fu;
+    const uint32_t x = BITS == 2 ? ((t & 1) ? sp.w[t >> 1] >> 8 : sp.w[t >> 1]) : sp.w[t];
+    u32x4 out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        out[r] = and_or(x >> raw_shift<DT, BITS>(r), kField << raw_pos<DT, BITS>(r), magic[r]);
+    }
+    return out;
+}
+
+template <int DT, int BITS, bool FC1, int KS, int P, bool RAW>
+__global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, DecodePlan q)
+{
+    constexpr Order O = RAW ? raw_order<BITS>() : code_order<DT, BITS>();
+    constexpr int kBlocksWG = kWavesS / KS;             // 16-row weight blocks per workgroup
+    constexpr int kRowsWG = 16 * kBlocksWG;             // weight rows per workgroup
+    constexpr int SPP = kLine * 8 / BITS / kSuperK;     // super-steps per piece
+    static_assert(BITS == 2 || BITS == 4, "a 128-byte line holds whole super-steps");
+    static_assert(!FC1 || KS == 1, "fc1 pairs gate and up columns within one wavefront");
+    __shared__ __attribute__((aligned(16))) uint32_t a_tile[kRowsA * kPitchA];
+    __shared__ __attribute__((aligned(16))) uint8_t b_slot[kWavesS][16 * kSlotPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t sc_tab[kRowsWG * kScPitch];
+    __shared__ float a_sum[kRowsA][kMaxSuper];  // RAW: -sum (b_r + zp) a of A row m over super-step s
+    __shared__ __attribute__((aligned(16))) float m_sum[kMaxSuper][kRowsA];  // RAW: the same by MFMA row
+    __shared__ __attribute__((aligned(16))) float red[KS == 2 ? kBlocksWG * kWave * 4 : 4];
+    __shared__ int s_e[kRowsA];     // fc1: expert of route r
+    __shared__ int s_arow[kRowsA];  // fc1: A tile row (token) of the expert's m-th route
+    __shared__ int s_info[2];       // fc1: first sorted position, route count
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const int rb = wave % kBlocksWG;  // the wavefront's weight row block
+    const int kp = wave / kBlocksWG;  // its share of K
+    const int K = p.K;
+    const int KW = K / KS;            // inputs per wavefront
+    const int s0 = kp * (KW / kSuperK);  // its first super-step
+    const int n_super = KW / kSuperK;
+    const int n_blocks = K / p.block_size;
+    const int bs_shift = __builtin_ctz((unsigned)p.block_size);  // a power of two
+    const int nt = p.N / kRowsWG;
+    const int e = blockIdx.x / nt;
+    const int n = blockIdx.x - e * nt;
+    const int row_bytes = K * BITS / 8;
+    const int wr0 = n * kRowsWG + 16 * rb;  // first weight row of the block within the expert
+    const int col0 = FC1 ? wr0 / 2 : wr0;   // first output column (fc1: 8 activation columns)
+    const uint16_t* a_src = reinterpret_cast<const uint16_t*>(p.a);
+    uint32_t magic[4];  // RAW: per-register bases
+#pragma unroll
+    for (int r = 0; r < 4; ++r) magic[r] = opaque(raw_magic<DT, BITS>(r));
+    const float zp = held(p.w.zp_fallback);
+    const int act = held(p.act);
+    uint16_t* const act_out = held(reinterpret_cast<uint16_t*>(p.act_out));
+    float* const y2 = held(p.y2);
+
+    // Every load below is issued unconditionally (indices clamped): a load
+    // under a branch leaves its register undefined on the other path, and the
+    // compiler then waits for it on the spot.
+    // 0) fc1: router logits of tokens wave and wave + 8; fc2: the expert's
+    //    rows in the sorted order (written by fc1) and their route ids
+    float lg[kTokW];
+    int first = 0, count = 0;
+    int y2_row[4] = {0, 0, 0, 0};  // fc2: route ids of rows 4g..4g+3 (clamped)
+    if constexpr (FC1) {
+#pragma unroll
+        for (int j = 0; j < kTokW; ++j) {
+            const int t = min(wave + kWavesS * j, q.T - 1);
+            lg[j] = q.logits[(int64_t)t * q.E + min(lane, q.E - 1)];
+        }
+    } else {
+        first = q.offsets[e];
+        count = q.offsets[e + 1] - first;
+        if (count == 0) return;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y2_row[i] = q.sorted[first + min(4 * g + i, count - 1)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 1) scale table: 16-byte units of 8 blocks, row-major over the workgroup's rows
+    const uint16_t* sc_src =
+        reinterpret_cast<const uint16_t*>(p.w.scales) + ((int64_t)e * p.N + n * kRowsWG) * n_blocks;
+    const int upr = n_blocks >> 3;  // units per row
+    const int n_units = kRowsWG * upr;
+    u32x4 sc_unit[kScUnits];
+#pragma unroll
+    for (int k = 0; k < kScUnits; ++k) {
+        const int u = min(tid + kThreadsS * k, n_units - 1);
+        const int r = u / upr;
+        sc_unit[k] = *reinterpret_cast<const u32x4*>(sc_src + r * n_blocks + 8 * (u - r * upr));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2) A row `wave` (rows 8.. follow the weights, below): 16-byte chunk
+    //    lane + 64*qq, so each load reads whole lines
+    const int a_rows = FC1 ? q.T : count;
+    const int cpr = K / 8;  // 16-byte chunks per A row (a multiple of 16)
+    u32x4 av[4];
+    auto load_a = [&](int m) {
+        const uint16_t* row = a_src + (int64_t)(FC1 ? min(m, a_rows - 1) : first + min(m, a_rows - 1)) * K;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            av[qq] = *reinterpret_cast<const u32x4*>(row + 8 * min(lane + kWave * qq, cpr - 1));
+        }
+    };
+    load_a(wave);
+    // every early load of the workgroup (one per CU) is queued before any
+    // weight load: requests return in order, and an L2 hit queued behind
+    // weight misses waits for them
+    __syncthreads();
+
+    // 3) every packed weight byte of the wavefront: piece j, load i reads rows
+    //    8i + lane/8 of the block, bytes [128j + 16*(lane%8), +16) of its K
+    //    share (clamped into the share past its end; those super-steps are
+    //    skipped)
+    const int kb0 = s0 * kSuperK * BITS / 8;  // first byte of the share in a row
+    const int kbw = KW * BITS / 8;            // bytes of the share
+    const uint8_t* wcodes = p.w.codes + ((int64_t)e * p.N + wr0) * row_bytes + kb0;
+    const int lrow = lane >> 3;
+    const int lbyte = 16 * (lane & 7);
+    u32x4 bv[P][2];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ob = min(kLine * j + lbyte, kbw - 16);
+            bv[j][i] = *reinterpret_cast<const u32x4*>(wcodes + (8 * i + lrow) * row_bytes + ob);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 4) fc1: route every token while the weights are in flight; this
+    //    expert's routes in ascending order, and their first sorted position
+    if constexpr (FC1) {
+        const int R = q.T * p.top_k;
+        const bool writer = blockIdx.x == 0;
+#pragma unroll
+        for (int j = 0; j < kTokW; ++j) {
+            const int t = wave + kWavesS * j;
+            if (t >= q.T) break;
+            route_values<1>(q.E, p.top_k, q.normalize, [&](int) { return lg[j]; },
+                            [&](int slot, int ex, float w) {
+                                const int r = t * p.top_k + slot;
+                                s_e[r] = ex;
+                                if (writer) {
+                                    q.weights[r] = w;
+                                    if (q.ids_out) q.ids_out[r] = ex;
+                                    if (q.w_out) q.w_out[r] = w;
+                                }
+                            });
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const int ex = lane < R ? s_e[lane] : -1;
+            const uint64_t mine = __ballot(ex == e);
+            const uint64_t below = __ballot(lane < R && ex < e);
+            if (ex == e) s_arow[__popcll(mine & ((1ull << lane) - 1ull))] = lane / p.top_k;
+            if (lane == 0) {
+                s_info[0] = __popcll(below);
+                s_info[1] = __popcll(mine);
+            }
+            if (writer) {  // offsets and sorted routes of every expert, for fc2 and the combine
+                if (lane < R) {
+                    int less = 0, same_before = 0;
+                    for (int r = 0; r < R; ++r) {
+                        const int o = s_e[r];
+                        less += o < ex;
+                        same_before += (o == ex) & (r < lane);
+                    }
+                    q.sorted[less + same_before] = lane;
+                }
+                // no loop around the stores: the compiler would drain every
+                // load in flight before entering it
+                if (lane < q.E) {
+                    int less = 0;
+                    for (int r = 0; r < R; ++r) less += s_e[r] < lane;
+                    q.offsets[lane] = less;
+                }
+                if (lane == 0) q.offsets[q.E] = R;
+            }
+        }
+        __syncthreads();
+        first = s_info[0];
+        count = s_info[1];
+        if (count == 0) return;  // whole workgroup; the weight loads drain on their own
+    }
+
+    // 5) A tile (permuted to the MFMA register order; int2 pairs the chunks of
+    //    lanes l and l^1, both in the same row), the row sums of its
+    //    super-steps (RAW) and the scale table to LDS
+    auto store_a = [&](int m) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int ch = lane + kWave * qq;
+            u32x4 v;
+            if constexpr (O == Order::kStride8) v = permute_chunk_pair(av[qq], lane & 1);
+            else v = permute_chunk<O>(av[qq]);
+            if constexpr (RAW) {  // -sum (b_r + zp) a over the super-step; 16 lanes hold one
+                float part = 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float coef = -(raw_base<DT, BITS>(r) + zp);
+                    part += coef * Dt<DT>::to_float((uint16_t)(v[r] & 0xffffu));
+                    part += coef * Dt<DT>::to_float((uint16_t)(v[r] >> 16));
+                }
+                part += dpp_f32<kDppXor1>(part);
+                part += dpp_f32<kDppXor2>(part);
+                part += dpp_f32<kDppHalfMirror>(part);
+                part += dpp_f32<kDppMirror>(part);
+                if (m < a_rows && ch < cpr && c == 0) a_sum[m][ch >> 4] = part;
+            }
+            if (m < a_rows && ch < cpr) *reinterpret_cast<u32x4*>(a_tile + m * kPitchA + 4 * ch) = v;
+        }
+    };
+    store_a(wave);
+    if (a_rows > kWavesS) {  // rows 8..15: loaded after the weights, so they wait for them
+        load_a(wave + kWavesS);
+        store_a(wave + kWavesS);
+    }
+#pragma unroll
+    for (int k = 0; k < kScUnits; ++k) {
+        const int u = tid + kThreadsS * k;
+        if (u < n_units) {
+            const int r = u / upr;
+            uint32_t* dst = reinterpret_cast<uint32_t*>(sc_tab + r * kScPitch + 8 * (u - r * upr));
+            *reinterpret_cast<u32x2*>(dst) = u32x2{sc_unit[k].x, sc_unit[k].y};
+            *reinterpret_cast<u32x2*>(dst + 2) = u32x2{sc_unit[k].z, sc_unit[k].w};
+        }
+    }
+    __syncthreads();
+    const bool row_ok = c < count;
+    const int arow = row_ok ? (FC1 ? s_arow[c] : c) : 0;
+    if constexpr (RAW) {  // corrections by MFMA row: m_sum[s][m] = a_sum[A row of route m][s]
+        if (tid < kMaxSuper * kRowsA) {
+            const int s = tid >> 4, m = tid & 15;
+            m_sum[s][m] = m < count ? a_sum[FC1 ? s_arow[m] : m][s] : 0.f;
+        }
+        __syncthreads();
+    }
+
+    // 6) the pieces, each as soon as it lands
+    const uint32_t* a_row = a_tile + arow * kPitchA;
+    // MFMA column c of the block: fc1 gate row 2c (c < 8) or up row 2(c-8)+1,
+    // stored in slot c; fc2 row c
+    const int wrow = FC1 ? 2 * (c & 7) + (c >> 3) : c;
+    const uint16_t* sc_row = sc_tab + (16 * rb + wrow) * kScPitch;
+    uint8_t* slot = b_slot[wave];
+    const int lslot = FC1 ? (lrow >> 1) + 8 * (lrow & 1) : lrow;  // slot of row lrow (+4 for load 1 in fc1)
+
+    f32x4 acc[SPP];  // one accumulator per super-step of a piece: independent MFMA chains
+#pragma unroll
+    for (int sp = 0; sp < SPP; ++sp) acc[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A fragments: only lanes of real rows read them; the others keep stale
+    // values, which reach only MFMA rows that are never stored.  A skipped
+    // super-step (past the K share) keeps them too and is cancelled by a zero
+    // scale.
+    u32x4 a4[SPP][4];
+#pragma unroll
+    for (int sp = 0; sp < SPP; ++sp)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a4[sp][t] = u32x4{0u, 0u, 0u, 0u};
+
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        if (j * SPP >= n_super) break;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            // row 8i + lrow: fc1 slot (row >> 1) + 8 * (row & 1) = 4i + lslot
+            *reinterpret_cast<u32x4*>(slot + (FC1 ? 4 * i + lslot : 8 * i + lrow) * kSlotPitch + lbyte) = bv[j][i];
+        }
+        // gather the piece: A fragments, spans, row sums and scales
+        Span<BITS> spn[SPP];
+        f32x4 rs[SPP];
+        float scl[SPP];
+#pragma unroll
+        for (int sp = 0; sp < SPP; ++sp) {
+            const int s = j * SPP + sp;
+            const bool ok = s < n_super;  // uniform
+            const int S = s0 + min(s, n_super - 1);  // the super-step in K
+            if (ok && row_ok) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    a4[sp][t] = *reinterpret_cast<const u32x4*>(a_row + (S * kSuperK + 32 * g) / 2 + 4 * t);
+                }
+            }
+            spn[sp] = load_span<BITS>(slot + c * kSlotPitch, sp * kSuperK + 32 * g);
+            const float sv = Dt<DT>::to_float(sc_row[(S * kSuperK + (RAW ? 0 : 32 * g)) >> bs_shift]);
+            scl[sp] = ok ? sv : 0.f;
+            if constexpr (RAW) rs[sp] = *reinterpret_cast<const f32x4*>(&m_sum[S][4 * g]);
+        }
+        if constexpr (RAW) {
+            f32x4 part[SPP];
+#pragma unroll
+            for (int sp = 0; sp < SPP; ++sp) part[sp] = rs[sp];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int sp = 0; sp < SPP; ++sp)
+                    part[sp] = Dt<DT>::mfma(a4[sp][t], raw_step_based<DT, BITS>(spn[sp], t, magic), part[sp]);
+#pragma unroll
+            for (int sp = 0; sp < SPP; ++sp) acc[sp] += part[sp] * scl[sp];
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int sp = 0; sp < SPP; ++sp) {
+                    BlockParams bq;
+                    bq.zp = zp;
+                    bq.scale = scl[sp];
+                    acc[sp] = Dt<DT>::mfma(a4[sp][t], dequant_zp<DT, BITS, kZpConst>(spn[sp], t, bq), acc[sp]);
+                }
+        }
+    }
+    f32x4 sum = acc[0];
+#pragma unroll
+    for (int sp = 1; sp < SPP; ++sp) sum += acc[sp];
+
+    // 7) epilogue: lane (g, c) holds MFMA rows 4g..4g+3 of column c
+    if constexpr (KS == 2) {  // the second K share hands its sums to the first
+        f32x4* r4 = reinterpret_cast<f32x4*>(red) + rb * kWave + lane;
+        if (kp == 1) *r4 = sum;
+        __syncthreads();
+        if (kp == 1) return;
+        sum += *r4;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = 4 * g + i;
+        if constexpr (FC1) {
+            const float up = dpp_f32<kDppRor8>(sum[i]);  // column c + 8: the up row of column c
+            if (m < count && c < 8) {
+                const int I = p.N / 2;
+                uint16_t* out = act_out + (int64_t)(first + m) * I;
+                out[col0 + c] = Dt<DT>::from_float(act_value<DT>(act, sum[i], up));
+            }
+        } else {
+            if (m < count) y2[(int64_t)y2_row[i] * p.N + col0 + c] = sum[i];
+        }
+    }
+}
+
+template <bool FC1, int DT, int BITS, int KS, int P, bool RAW>
+hipError_t run(const ProjLaunch& p, const DecodePlan& plan, hipStream_t s)
+{
+    const int rows_wg = 16 * kWavesS / KS;
+    launch(stream_kernel<DT, BITS, FC1, KS, P, RAW>, dim3((unsigned)(plan.E * (p.N / rows_wg))),
+           dim3(kThreadsS), s, p, plan);
+    return hipGetLastError();
+}
+
+template <bool FC1, int DT, int BITS, int KS, bool RAW>
+hipError_t launch_pieces(const ProjLaunch& p, const DecodePlan& plan, hipStream_t s)
+{
+    const int pieces = (p.K / KS * BITS / 8 + kLine - 1) / kLine;
+    if (pieces <= 1) return run<FC1, DT, BITS, KS, 1, RAW>(p, plan, s);
+    if (pieces <= 2) return run<FC1, DT, BITS, KS, 2, RAW>(p, plan, s);
+    if (pieces <= 4) return run<FC1, DT, BITS, KS, 4, RAW>(p, plan, s);
+    if constexpr (BITS == 4 && KS == 1) {
+        if (pieces <= 8) return run<FC1, DT, BITS, KS, 8, RAW>(p, plan, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool FC1, int DT, int BITS, bool RAW>
+hipError_t launch_split(const ProjLaunch& p, const DecodePlan& plan, hipStream_t s)
+{
+    if constexpr (!FC1) {
+        if (p.K % (2 * kSuperK) == 0) return launch_pieces<FC1, DT, BITS, 2, RAW>(p, plan, s);
+    }
+    return launch_pieces<FC1, DT, BITS, 1, RAW>(p, plan, s);
+}
+
+template <bool FC1, int DT>
+hipError_t launch_stream(const ProjLaunch& p, const DecodePlan& plan, hipStream_t s)
+{
+    if (!stream_fits(p.w, p.K, p.N, p.block_size, FC1)) return hipErrorInvalidValue;
+    const bool raw = p.block_size % kSuperK == 0;
+    if (p.w.bits == 2) {
+        return raw ? launch_split<FC1, DT, 2, true>(p, plan, s) : launch_split<FC1, DT, 2, false>(p, plan, s);
+    }
+    return raw ? launch_split<FC1, DT, 4, true>(p, plan, s) : launch_split<FC1, DT, 4, false>(p, plan, s);
+}
+
+}  // namespace
+
+bool stream_fits(const ProjArgs& w, int K, int N, int block_size, bool fc1)
+{
+    (void)fc1;
+    const int bs = block_size;
+    return (w.bits == 2 || w.bits == 4) && w.zp == nullptr && K <= kMaxK && K % kSuperK == 0 &&
+           N % (16 * kWavesS) == 0 && bs >= 32 && (bs & (bs - 1)) == 0 && (K / bs) % 8 == 0 &&
+           K / bs <= kMaxBlocks && reinterpret_cast<uintptr_t>(w.scales) % 16 == 0 &&
+           (bs % kSuperK == 0 || w.fast);  // RAW takes any constant zero point
+}
+
+hipError_t launch_fc1_stream(const ProjLaunch& p, const DecodePlan& plan, int dtype, hipStream_t s)
+{
+    if (plan.T > kRowsA || plan.T * p.top_k > kRowsA || plan.E > kWave) return hipErrorInvalidValue;
+    return dtype == kBF16 ? launch_stream<true, kBF16>(p, plan, s) : launch_stream<true, kF16>(p, plan, s);
+}
+
+hipError_t launch_fc2_stream(const ProjLaunch& p, const DecodePlan& plan, int dtype, hipStream_t s)
+{
+    if (plan.T * p.top_k > kRowsA) return hipErrorInvalidValue;
+    return dtype == kBF16 ? launch_stream<false, kBF16>(p, plan, s) : launch_stream<false, kF16>(p, plan, s);
+}
+
+}  // namespace qmoe

@@ -359,11 +359,17 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     // Chosen when every expert is likely selected, K fits one chunk and fc1's
     // block of weights fits the kernel's LDS staging (2-bit codes, no
     // zero-point tensor: the other variants run out of registers).
-    const bool expert_mode = L.decode && E <= 64 && E <= R && H <= 2048 && I <= 2048 &&
-                             fc1->bits == 2 && fc1->zero_points == nullptr;
+    // Streamed decode (at most 16 expanded rows): the same idea with every
+    // wavefront owning whole weight rows and consuming its weights piece by
+    // piece as they arrive.
+    const bool stream_mode = L.decode && R <= 16 && E <= 64 && E <= R &&
+                             qmoe::stream_fits(w1, H, 2 * I, block_size, true) &&
+                             qmoe::stream_fits(w2, I, H, block_size, false);
+    const bool expert_mode = !stream_mode && L.decode && E <= 64 && E <= R && H <= 2048 &&
+                             I <= 2048 && fc1->bits == 2 && fc1->zero_points == nullptr;
     qmoe::DecodePlan plan{logits, (int)T, E, normalize, w, topk_ids_out, topk_w_out, offsets, sorted};
     const qmoe::DecodePlan* dplan = expert_mode ? &plan : nullptr;
-    if (L.decode && !expert_mode) {  // routing, grouping and the m-tile list in one launch
+    if (L.decode && !expert_mode && !stream_mode) {  // routing, grouping and the m-tile list in one launch
         timer_begin(QMOE_STAGE_ROUTE, s);
         e = qmoe::launch_decode_plan(logits, (int)T, E, top_k, normalize, w, topk_ids_out,
                                      topk_w_out, wl1, n1, s);
@@ -398,7 +404,9 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     p1.act = activation;
     p1.act_out = act;
     timer_begin(QMOE_STAGE_FC1, s);
-    e = L.decode ? qmoe::launch_fc1_decode(p1, dplan, dtype, s) : qmoe::launch_fc1_prefill(p1, dtype, s);
+    e = stream_mode ? qmoe::launch_fc1_stream(p1, plan, dtype, s)
+        : L.decode  ? qmoe::launch_fc1_decode(p1, dplan, dtype, s)
+                    : qmoe::launch_fc1_prefill(p1, dtype, s);
     timer_end(QMOE_STAGE_FC1, s);
     if (e != hipSuccess) return hip_fail(e, "fc1 launch");
 
@@ -417,7 +425,9 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     p2.grid = L.cap2 > 0 ? L.cap2 : 1;
     p2.y2 = y2;
     timer_begin(QMOE_STAGE_FC2, s);
-    e = L.decode ? qmoe::launch_fc2_decode(p2, dplan, dtype, s) : qmoe::launch_fc2_prefill(p2, dtype, s);
+    e = stream_mode ? qmoe::launch_fc2_stream(p2, plan, dtype, s)
+        : L.decode  ? qmoe::launch_fc2_decode(p2, dplan, dtype, s)
+                    : qmoe::launch_fc2_prefill(p2, dtype, s);
     timer_end(QMOE_STAGE_FC2, s);
     if (e != hipSuccess) return hip_fail(e, "fc2 launch");
 

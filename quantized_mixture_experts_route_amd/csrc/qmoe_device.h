@@ -478,23 +478,26 @@ __device__ inline float gated(float g, float u)
 namespace qmoe {
 
 // ---------------------------------------------------------------- wave reductions
-// Cross-lane exchange within 32-lane halves through ds_swizzle's bit-mask
-// mode (lane i reads lane i ^ XOR); the two halves are then joined with
-// readlane.  Every lane of the wave must be active.
-template <int XOR>
-__device__ inline uint32_t swizzle_xor(uint32_t v)
+// Cross-lane exchange within 16-lane rows by DPP (a VALU operand modifier,
+// no LDS round trip): lane i ^ 1 and lane i ^ 2 by quad permutes, then the
+// 8-lane and 16-lane mirrors, which pair each lane with one of the other
+// half once every quad (then every 8 lanes) holds its combined value.  The
+// four rows are joined with readlane.  Every lane of the wave must be active.
+enum : int { kDppXor1 = 0xb1, kDppXor2 = 0x4e, kDppHalfMirror = 0x141, kDppMirror = 0x140 };
+
+template <int CTRL>
+__device__ inline uint32_t dpp_u32(uint32_t v)
 {
-    static_assert(XOR > 0 && XOR < 32, "ds_swizzle bit-mask mode spans 32 lanes");
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1f | (XOR << 10));
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
 }
 
 __device__ inline uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-template <int XOR>
-__device__ inline uint64_t swizzle_xor_u64(uint64_t v)
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t v)
 {
-    const uint32_t lo = swizzle_xor<XOR>((uint32_t)v);
-    const uint32_t hi = swizzle_xor<XOR>((uint32_t)(v >> 32));
+    const uint32_t lo = dpp_u32<CTRL>((uint32_t)v);
+    const uint32_t hi = dpp_u32<CTRL>((uint32_t)(v >> 32));
     return ((uint64_t)hi << 32) | lo;
 }
 
@@ -508,36 +511,46 @@ __device__ inline uint64_t readlane_u64(uint64_t v, int lane)
 // Wave-wide maximum of an unsigned 64-bit word, returned to every lane.
 __device__ inline uint64_t wave_max_u64(uint64_t v)
 {
-    v = max_u64(v, swizzle_xor_u64<1>(v));
-    v = max_u64(v, swizzle_xor_u64<2>(v));
-    v = max_u64(v, swizzle_xor_u64<4>(v));
-    v = max_u64(v, swizzle_xor_u64<8>(v));
-    v = max_u64(v, swizzle_xor_u64<16>(v));
-    return max_u64(readlane_u64(v, 0), readlane_u64(v, 32));
+    v = max_u64(v, dpp_u64<kDppXor1>(v));
+    v = max_u64(v, dpp_u64<kDppXor2>(v));
+    v = max_u64(v, dpp_u64<kDppHalfMirror>(v));
+    v = max_u64(v, dpp_u64<kDppMirror>(v));
+    return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)),
+                   max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 
-__device__ inline float swz_f32_max(float v, float o) { return o > v ? o : v; }
+__device__ inline float f32_max(float v, float o) { return o > v ? o : v; }
+
+template <int CTRL>
+__device__ inline float dpp_f32(float v)
+{
+    return __builtin_bit_cast(float, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+}
+
+__device__ inline float readlane_f32(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
 
 // Wave-wide maximum of NaN-free floats.
 __device__ inline float wave_max_f32(float v)
 {
-#define QMOE_STEP(X) v = swz_f32_max(v, __builtin_bit_cast(float, swizzle_xor<X>(__builtin_bit_cast(uint32_t, v))))
-    QMOE_STEP(1); QMOE_STEP(2); QMOE_STEP(4); QMOE_STEP(8); QMOE_STEP(16);
-#undef QMOE_STEP
-    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-    return swz_f32_max(a, b);
+    v = f32_max(v, dpp_f32<kDppXor1>(v));
+    v = f32_max(v, dpp_f32<kDppXor2>(v));
+    v = f32_max(v, dpp_f32<kDppHalfMirror>(v));
+    v = f32_max(v, dpp_f32<kDppMirror>(v));
+    return f32_max(f32_max(readlane_f32(v, 0), readlane_f32(v, 16)),
+                   f32_max(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
-// Wave-wide float sum (butterfly order), returned to every lane.
+// Wave-wide float sum (a fixed pairing order), returned to every lane.
 __device__ inline float wave_sum_f32(float v)
 {
-#define QMOE_STEP(X) v += __builtin_bit_cast(float, swizzle_xor<X>(__builtin_bit_cast(uint32_t, v)))
-    QMOE_STEP(1); QMOE_STEP(2); QMOE_STEP(4); QMOE_STEP(8); QMOE_STEP(16);
-#undef QMOE_STEP
-    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-    return a + b;
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppHalfMirror>(v);
+    v += dpp_f32<kDppMirror>(v);
+    return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
 }
 
 }  // namespace qmoe

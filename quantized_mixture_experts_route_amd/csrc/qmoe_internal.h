@@ -120,6 +120,14 @@ hipError_t launch_fc2_prefill(const ProjLaunch& p, int dtype, hipStream_t s);
 hipError_t launch_fc1_decode(const ProjLaunch& p, const DecodePlan* plan, int dtype, hipStream_t s);
 hipError_t launch_fc2_decode(const ProjLaunch& p, const DecodePlan* plan, int dtype, hipStream_t s);
 
+// Streamed decode projections (R = T*top_k <= 16, E <= 64): every expert's
+// weights requested at launch and consumed piece by piece as they land; fc1
+// routes the tokens itself and writes the plan.  stream_fits: the projection's
+// shapes, widths and scales suit the kernel.
+bool stream_fits(const ProjArgs& w, int K, int N, int block_size, bool fc1);
+hipError_t launch_fc1_stream(const ProjLaunch& p, const DecodePlan& plan, int dtype, hipStream_t s);
+hipError_t launch_fc2_stream(const ProjLaunch& p, const DecodePlan& plan, int dtype, hipStream_t s);
+
 hipError_t launch_combine(const float* y2, const float* weights, int64_t T, int H, int top_k,
                           void* out, int dtype, hipStream_t s);
 

@@ -265,6 +265,45 @@ def test_layer_decode_expert_stationary(T, k, E, skew):
     _layer_check(spec, 40 + T + E, logits=logits)
 
 
+# Streamed decode: R = T*top_k <= 16, E <= R, 2/4-bit widths, K <= 2048 with
+# whole 8-block scale units per row; cases cover both widths per projection,
+# RAW (block multiple of 128) and per-element dequant, one piece with a
+# clamped tail (K = 256 at 2 bits), eight pieces (4 bits, K = 2048), A rows
+# 8..15 loaded after the weights (fc1 T = 16; fc2 16 rows on one expert) and
+# an expert nobody selected.
+STREAM = [
+    dict(T=8, H=2048, I=2048, E=8, k=2, fc1_bits=2, fc2_bits=2, block_size=128, dtype=1, act=1,
+         zp_mode="zpo", zpo=1.5),
+    dict(T=1, H=1024, I=512, E=2, k=2, fc1_bits=4, fc2_bits=2, block_size=64, dtype=2, act=0,
+         zp_mode="sym", zpo=math.nan),
+    dict(T=5, H=512, I=1024, E=6, k=3, fc1_bits=2, fc2_bits=4, block_size=32, dtype=1, act=0,
+         zp_mode="sym", zpo=math.nan),
+    dict(T=16, H=256, I=512, E=16, k=1, fc1_bits=4, fc2_bits=4, block_size=32, dtype=2, act=1,
+         zp_mode="sym", zpo=math.nan),
+    dict(T=3, H=2048, I=2048, E=2, k=2, fc1_bits=2, fc2_bits=2, block_size=256, dtype=2, act=0,
+         zp_mode="zpo", zpo=1.5),
+    dict(T=7, H=2048, I=1024, E=4, k=2, fc1_bits=4, fc2_bits=4, block_size=128, dtype=1, act=1,
+         zp_mode="sym", zpo=math.nan),
+    dict(T=4, H=256, I=256, E=4, k=2, fc1_bits=2, fc2_bits=2, block_size=32, dtype=2, act=1,
+         zp_mode="zpo", zpo=1.5),
+]
+
+
+@pytest.mark.parametrize("case", range(len(STREAM)))
+def test_layer_stream_decode(case):
+    spec = synth.custom(name=f"stream{case}", **STREAM[case])
+    _layer_check(spec, 1300 + case)
+
+
+def test_layer_stream_decode_one_expert_sixteen_rows():
+    # every token on expert 0: fc2 stages 16 rows of one expert; expert 1 exits
+    spec = synth.custom(T=16, H=512, I=256, E=2, k=1, fc1_bits=2, fc2_bits=4, block_size=32,
+                        dtype=1, act=0, zp_mode="zpo", zpo=1.5, name="stream_one_expert")
+    logits = np.zeros((16, 2), dtype=np.float32)
+    logits[:, 0] = 2.0
+    _layer_check(spec, 1350, logits=logits)
+
+
 @pytest.mark.parametrize("T", [5, 300])
 def test_layer_all_tokens_one_expert(T):
     spec = synth.custom(T=T, H=256, I=256, E=8, k=1, fc1_bits=3, fc2_bits=4, block_size=32,
