@@ -1,5 +1,5 @@
-// gemm_stream.hip -- decode projections that request every expert's packed
-// weights at launch and consume them as they land.
+// gemm_stream.hip -- decode projections that stream every selected expert's
+// packed weights and consume them piece by piece as they land.
 //
 // [PR 33569: the decode path serves small expanded-row counts, and its time
 // is set by the packed-weight bytes; qmoe.rs QMoEKernel::execute: route,
@@ -14,20 +14,25 @@
 // reduced across wavefronts.  fc2 (KS = 2 when K allows): 64 rows per
 // workgroup and two wavefronts per block, whose partial sums meet once in LDS.
 //
-// Issue order (vmcnt retires loads in issue order, so each wait covers the
-// loads it needs and no later ones; scheduling barriers keep the groups in
-// place, and a workgroup barrier puts every early load of the CU ahead of
-// every weight load, since an L2 hit queued behind misses waits for them): fc1 the router logits of the wavefront's tokens, fc2 the expert's
-// offsets and route ids; the scale table of the workgroup's rows; one A row
-// per wavefront (fc1 the tokens, all of them, since routing is not known yet;
-// fc2 the expert's rows); then every packed weight byte of the wavefront, in
-// P pieces of one 128-byte line per row, eight whole lines per load
-// instruction.  fc1 routes while the weights are in flight, and the first
-// workgroup writes the routing weights, expert offsets and sorted routes for
-// fc2 and the combine.  Piece j is consumed as soon as it lands: copied to a
-// wavefront-private LDS slot, read back as MFMA spans, and multiplied with the
-// A fragments of its super-steps, whose MFMA chains are interleaved so that
-// one wavefront keeps the matrix core busy.
+// Order: fc1 loads the router logits of the wavefront's tokens, fc2 the
+// expert's offsets and route ids; then the scale table of the workgroup's
+// rows, one A row per wavefront (fc1 the tokens, all of them, since routing
+// is not known yet; fc2 the expert's rows) and the first two weight pieces of
+// the wavefront's block (one piece: one 128-byte line of each of its 16 rows,
+// eight whole lines per load instruction).  The workgroup's shared work
+// comes next: fc1 routes every token (the first workgroup writes the routing
+// weights, expert offsets and sorted routes for fc2 and the combine), and A,
+// its per-super-step corrections and the scales go to LDS.  Then each
+// wavefront requests the rest of its pieces and waits for no other wavefront
+// until fc2's two K shares meet at the end: requests are accepted only as
+// fast as earlier data returns, so a workgroup barrier after them would hold
+// every wavefront until the slowest had issued.  vmcnt retires loads in issue
+// order, so each wait names exactly its own loads (and an L2 hit issued after
+// the weight misses would wait for them: the small loads go first).  Piece j
+// is consumed as soon as it lands: copied to a wavefront-private LDS slot,
+// read back as MFMA spans, and multiplied with the A fragments of its
+// super-steps, whose MFMA chains are interleaved.  Scheduling barriers keep
+// the load groups in this order.
 //
 // MFMA mapping and dequantization are those of the other projection kernels:
 // lane 16g + c feeds A row c (a routed row; zeros past the expert's rows,
@@ -130,6 +135,7 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
     constexpr int kBlocksWG = kWavesS / KS;             // 16-row weight blocks per workgroup
     constexpr int kRowsWG = 16 * kBlocksWG;             // weight rows per workgroup
     constexpr int SPP = kLine * 8 / BITS / kSuperK;     // super-steps per piece
+    constexpr int kEarly = P < 2 ? P : 2;               // pieces requested before the shared work
     static_assert(BITS == 2 || BITS == 4, "a 128-byte line holds whole super-steps");
     static_assert(!FC1 || KS == 1, "fc1 pairs gate and up columns within one wavefront");
     __shared__ __attribute__((aligned(16))) uint32_t a_tile[kRowsA * kPitchA];
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2) A row `wave` (rows 8.. follow the weights, below): 16-byte chunk
+    // 2) A row `wave` (rows 8.. are loaded when staged): 16-byte chunk
     //    lane + 64*qq, so each load reads whole lines
     const int a_rows = FC1 ? q.T : count;
     const int cpr = K / 8;  // 16-byte chunks per A row (a multiple of 16)
@@ -220,33 +226,32 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
         }
     };
     load_a(wave);
-    // every early load of the workgroup (one per CU) is queued before any
-    // weight load: requests return in order, and an L2 hit queued behind
-    // weight misses waits for them
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 
-    // 3) every packed weight byte of the wavefront: piece j, load i reads rows
-    //    8i + lane/8 of the block, bytes [128j + 16*(lane%8), +16) of its K
-    //    share (clamped into the share past its end; those super-steps are
-    //    skipped)
+    // 3) the first kEarly weight pieces of the wavefront: piece j, load i
+    //    reads rows 8i + lane/8 of the block, bytes [128j + 16*(lane%8), +16)
+    //    of its K share (clamped into the share past its end; those
+    //    super-steps are skipped).  The rest follow once the workgroup's
+    //    shared work is done.
     const int kb0 = s0 * kSuperK * BITS / 8;  // first byte of the share in a row
     const int kbw = KW * BITS / 8;            // bytes of the share
     const uint8_t* wcodes = p.w.codes + ((int64_t)e * p.N + wr0) * row_bytes + kb0;
     const int lrow = lane >> 3;
     const int lbyte = 16 * (lane & 7);
     u32x4 bv[P][2];
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
+    auto load_piece = [&](int j) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int ob = min(kLine * j + lbyte, kbw - 16);
             bv[j][i] = *reinterpret_cast<const u32x4*>(wcodes + (8 * i + lrow) * row_bytes + ob);
         }
-    }
+    };
+#pragma unroll
+    for (int j = 0; j < kEarly; ++j) load_piece(j);
     __builtin_amdgcn_sched_barrier(0);
 
-    // 4) fc1: route every token while the weights are in flight; this
-    //    expert's routes in ascending order, and their first sorted position
+    // 4) fc1: route every token; this expert's routes in ascending order,
+    //    and their first sorted position
     if constexpr (FC1) {
         const int R = q.T * p.top_k;
         const bool writer = blockIdx.x == 0;
@@ -298,7 +303,7 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
         __syncthreads();
         first = s_info[0];
         count = s_info[1];
-        if (count == 0) return;  // whole workgroup; the weight loads drain on their own
+        if (count == 0) return;  // whole workgroup; its first pieces drain on their own
     }
 
     // 5) A tile (permuted to the MFMA register order; int2 pairs the chunks of
@@ -329,7 +334,7 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
         }
     };
     store_a(wave);
-    if (a_rows > kWavesS) {  // rows 8..15: loaded after the weights, so they wait for them
+    if (a_rows > kWavesS) {  // rows 8..15
         load_a(wave + kWavesS);
         store_a(wave + kWavesS);
     }
@@ -354,7 +359,12 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
         __syncthreads();
     }
 
-    // 6) the pieces, each as soon as it lands
+    // 6) the rest of the wavefront's weight pieces
+#pragma unroll
+    for (int j = kEarly; j < P; ++j) load_piece(j);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 7) the pieces, each as soon as it lands
     const uint32_t* a_row = a_tile + arow * kPitchA;
     // MFMA column c of the block: fc1 gate row 2c (c < 8) or up row 2(c-8)+1,
     // stored in slot c; fc2 row c
@@ -431,7 +441,7 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
 #pragma unroll
     for (int sp = 1; sp < SPP; ++sp) sum += acc[sp];
 
-    // 7) epilogue: lane (g, c) holds MFMA rows 4g..4g+3 of column c
+    // 8) epilogue: lane (g, c) holds MFMA rows 4g..4g+3 of column c
     if constexpr (KS == 2) {  // the second K share hands its sums to the first
         f32x4* r4 = reinterpret_cast<f32x4*>(red) + rb * kWave + lane;
         if (kp == 1) *r4 = sum;
