@@ -128,13 +128,132 @@ __device__ inline u32x4 raw_step_based(const Span<BITS>& sp, int t, const uint32
     return out;
 }
 
+// The piece loop of the streamed projections.  Piece j of bv (load i: rows
+// 8i + lane/8 of the 16-row block, 16 bytes at 16*(lane%8) of the piece)
+// lands in the wavefront's LDS slot, row r at slot row slot_of(r); then its
+// SPP super-steps run as independent MFMA chains.  a_row: this lane's A row
+// (row_ok: a real one); sc_row: the scale table row of MFMA column c;
+// corr(S): the RAW corrections of MFMA rows 4g..4g+3 at super-step S (s0 +
+// local index).  Lanes past the real rows keep stale A fragments, which reach
+// only MFMA rows that are never stored; a skipped super-step (past the K
+// share) keeps them too and is cancelled by a zero scale.  Returns the sum of
+// the chains.
+template <int DT, int BITS, int P, bool RAW, class SlotOf, class Corr>
+__device__ inline f32x4 consume_pieces(const u32x4 (&bv)[P][2], uint8_t* slot, SlotOf slot_of,
+                                       const uint32_t* a_row, bool row_ok, const uint16_t* sc_row,
+                                       Corr corr, int s0, int n_super, int bs_shift, float zp,
+                                       const uint32_t (&magic)[4])
+{
+    constexpr int SPP = kLine * 8 / BITS / kSuperK;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const int lrow = lane >> 3;
+    const int lbyte = 16 * (lane & 7);
+    f32x4 acc[SPP];
+#pragma unroll
+    for (int sp = 0; sp < SPP; ++sp) acc[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 a4[SPP][4];
+#pragma unroll
+    for (int sp = 0; sp < SPP; ++sp)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a4[sp][t] = u32x4{0u, 0u, 0u, 0u};
+
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        if (j * SPP >= n_super) break;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            *reinterpret_cast<u32x4*>(slot + slot_of(8 * i + lrow) * kSlotPitch + lbyte) = bv[j][i];
+        }
+        // gather the piece: A fragments, spans, corrections and scales
+        Span<BITS> spn[SPP];
+        f32x4 rs[SPP];
+        float scl[SPP];
+#pragma unroll
+        for (int sp = 0; sp < SPP; ++sp) {
+            const int s = j * SPP + sp;
+            const bool ok = s < n_super;  // uniform
+            const int S = s0 + min(s, n_super - 1);  // the super-step in K
+            if (ok && row_ok) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    a4[sp][t] = *reinterpret_cast<const u32x4*>(a_row + (S * kSuperK + 32 * g) / 2 + 4 * t);
+                }
+            }
+            spn[sp] = load_span<BITS>(slot + c * kSlotPitch, sp * kSuperK + 32 * g);
+            const float sv = Dt<DT>::to_float(sc_row[(S * kSuperK + (RAW ? 0 : 32 * g)) >> bs_shift]);
+            scl[sp] = ok ? sv : 0.f;
+            if constexpr (RAW) rs[sp] = corr(S);
+        }
+        if constexpr (RAW) {
+            f32x4 part[SPP];
+#pragma unroll
+            for (int sp = 0; sp < SPP; ++sp) part[sp] = rs[sp];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int sp = 0; sp < SPP; ++sp)
+                    part[sp] = Dt<DT>::mfma(a4[sp][t], raw_step_based<DT, BITS>(spn[sp], t, magic), part[sp]);
+#pragma unroll
+            for (int sp = 0; sp < SPP; ++sp) acc[sp] += part[sp] * scl[sp];
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int sp = 0; sp < SPP; ++sp) {
+                    BlockParams bq;
+                    bq.zp = zp;
+                    bq.scale = scl[sp];
+                    acc[sp] = Dt<DT>::mfma(a4[sp][t], dequant_zp<DT, BITS, kZpConst>(spn[sp], t, bq), acc[sp]);
+                }
+        }
+    }
+    f32x4 sum = acc[0];
+#pragma unroll
+    for (int sp = 1; sp < SPP; ++sp) sum += acc[sp];
+    return sum;
+}
+
+// The A staging of the streamed projections: one A row of 16-byte chunks
+// (chunk lane + 64*qq), permuted to the MFMA register order (int2 pairs the
+// chunks of lanes l and l^1, both in the same row) into LDS row `dst`, and
+// for RAW the row's per-super-step corrections -sum (b_r + zp) a (16 lanes
+// hold one super-step) stored through put(super-step, value).
+template <int DT, int BITS, bool RAW, class Put>
+__device__ inline void stage_a_row(const u32x4 (&av)[4], bool valid, int cpr, uint32_t* dst, float zp, Put put)
+{
+    constexpr Order O = RAW ? raw_order<BITS>() : code_order<DT, BITS>();
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+        const int ch = lane + kWave * qq;
+        u32x4 v;
+        if constexpr (O == Order::kStride8) v = permute_chunk_pair(av[qq], lane & 1);
+        else v = permute_chunk<O>(av[qq]);
+        if constexpr (RAW) {
+            float part = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float coef = -(raw_base<DT, BITS>(r) + zp);
+                part += coef * Dt<DT>::to_float((uint16_t)(v[r] & 0xffffu));
+                part += coef * Dt<DT>::to_float((uint16_t)(v[r] >> 16));
+            }
+            part += dpp_f32<kDppXor1>(part);
+            part += dpp_f32<kDppXor2>(part);
+            part += dpp_f32<kDppHalfMirror>(part);
+            part += dpp_f32<kDppMirror>(part);
+            if (valid && ch < cpr && (lane & 15) == 0) put(ch >> 4, part);
+        }
+        if (valid && ch < cpr) *reinterpret_cast<u32x4*>(dst + 4 * ch) = v;
+    }
+}
+
 template <int DT, int BITS, bool FC1, int KS, int P, bool RAW>
 __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, DecodePlan q)
 {
-    constexpr Order O = RAW ? raw_order<BITS>() : code_order<DT, BITS>();
     constexpr int kBlocksWG = kWavesS / KS;             // 16-row weight blocks per workgroup
     constexpr int kRowsWG = 16 * kBlocksWG;             // weight rows per workgroup
-    constexpr int SPP = kLine * 8 / BITS / kSuperK;     // super-steps per piece
     constexpr int kEarly = P < 2 ? P : 2;               // pieces requested before the shared work
     static_assert(BITS == 2 || BITS == 4, "a 128-byte line holds whole super-steps");
     static_assert(!FC1 || KS == 1, "fc1 pairs gate and up columns within one wavefront");
@@ -310,28 +429,8 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
     //    lanes l and l^1, both in the same row), the row sums of its
     //    super-steps (RAW) and the scale table to LDS
     auto store_a = [&](int m) {
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            const int ch = lane + kWave * qq;
-            u32x4 v;
-            if constexpr (O == Order::kStride8) v = permute_chunk_pair(av[qq], lane & 1);
-            else v = permute_chunk<O>(av[qq]);
-            if constexpr (RAW) {  // -sum (b_r + zp) a over the super-step; 16 lanes hold one
-                float part = 0.f;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float coef = -(raw_base<DT, BITS>(r) + zp);
-                    part += coef * Dt<DT>::to_float((uint16_t)(v[r] & 0xffffu));
-                    part += coef * Dt<DT>::to_float((uint16_t)(v[r] >> 16));
-                }
-                part += dpp_f32<kDppXor1>(part);
-                part += dpp_f32<kDppXor2>(part);
-                part += dpp_f32<kDppHalfMirror>(part);
-                part += dpp_f32<kDppMirror>(part);
-                if (m < a_rows && ch < cpr && c == 0) a_sum[m][ch >> 4] = part;
-            }
-            if (m < a_rows && ch < cpr) *reinterpret_cast<u32x4*>(a_tile + m * kPitchA + 4 * ch) = v;
-        }
+        stage_a_row<DT, BITS, RAW>(av, m < a_rows, cpr, a_tile + m * kPitchA, zp,
+                                   [&](int sstep, float v) { a_sum[m][sstep] = v; });
     };
     store_a(wave);
     if (a_rows > kWavesS) {  // rows 8..15
@@ -371,75 +470,11 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
     const int wrow = FC1 ? 2 * (c & 7) + (c >> 3) : c;
     const uint16_t* sc_row = sc_tab + (16 * rb + wrow) * kScPitch;
     uint8_t* slot = b_slot[wave];
-    const int lslot = FC1 ? (lrow >> 1) + 8 * (lrow & 1) : lrow;  // slot of row lrow (+4 for load 1 in fc1)
 
-    f32x4 acc[SPP];  // one accumulator per super-step of a piece: independent MFMA chains
-#pragma unroll
-    for (int sp = 0; sp < SPP; ++sp) acc[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // A fragments: only lanes of real rows read them; the others keep stale
-    // values, which reach only MFMA rows that are never stored.  A skipped
-    // super-step (past the K share) keeps them too and is cancelled by a zero
-    // scale.
-    u32x4 a4[SPP][4];
-#pragma unroll
-    for (int sp = 0; sp < SPP; ++sp)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) a4[sp][t] = u32x4{0u, 0u, 0u, 0u};
-
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-        if (j * SPP >= n_super) break;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            // row 8i + lrow: fc1 slot (row >> 1) + 8 * (row & 1) = 4i + lslot
-            *reinterpret_cast<u32x4*>(slot + (FC1 ? 4 * i + lslot : 8 * i + lrow) * kSlotPitch + lbyte) = bv[j][i];
-        }
-        // gather the piece: A fragments, spans, row sums and scales
-        Span<BITS> spn[SPP];
-        f32x4 rs[SPP];
-        float scl[SPP];
-#pragma unroll
-        for (int sp = 0; sp < SPP; ++sp) {
-            const int s = j * SPP + sp;
-            const bool ok = s < n_super;  // uniform
-            const int S = s0 + min(s, n_super - 1);  // the super-step in K
-            if (ok && row_ok) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    a4[sp][t] = *reinterpret_cast<const u32x4*>(a_row + (S * kSuperK + 32 * g) / 2 + 4 * t);
-                }
-            }
-            spn[sp] = load_span<BITS>(slot + c * kSlotPitch, sp * kSuperK + 32 * g);
-            const float sv = Dt<DT>::to_float(sc_row[(S * kSuperK + (RAW ? 0 : 32 * g)) >> bs_shift]);
-            scl[sp] = ok ? sv : 0.f;
-            if constexpr (RAW) rs[sp] = *reinterpret_cast<const f32x4*>(&m_sum[S][4 * g]);
-        }
-        if constexpr (RAW) {
-            f32x4 part[SPP];
-#pragma unroll
-            for (int sp = 0; sp < SPP; ++sp) part[sp] = rs[sp];
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int sp = 0; sp < SPP; ++sp)
-                    part[sp] = Dt<DT>::mfma(a4[sp][t], raw_step_based<DT, BITS>(spn[sp], t, magic), part[sp]);
-#pragma unroll
-            for (int sp = 0; sp < SPP; ++sp) acc[sp] += part[sp] * scl[sp];
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int sp = 0; sp < SPP; ++sp) {
-                    BlockParams bq;
-                    bq.zp = zp;
-                    bq.scale = scl[sp];
-                    acc[sp] = Dt<DT>::mfma(a4[sp][t], dequant_zp<DT, BITS, kZpConst>(spn[sp], t, bq), acc[sp]);
-                }
-        }
-    }
-    f32x4 sum = acc[0];
-#pragma unroll
-    for (int sp = 1; sp < SPP; ++sp) sum += acc[sp];
+    f32x4 sum = consume_pieces<DT, BITS, P, RAW>(
+        bv, slot, [&](int row) { return FC1 ? (row >> 1) + 8 * (row & 1) : row; }, a_row, row_ok, sc_row,
+        [&](int S) { return *reinterpret_cast<const f32x4*>(&m_sum[S][4 * g]); }, s0, n_super, bs_shift, zp,
+        magic);
 
     // 8) epilogue: lane (g, c) holds MFMA rows 4g..4g+3 of column c
     if constexpr (KS == 2) {  // the second K share hands its sums to the first
@@ -464,6 +499,7 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
         }
     }
 }
+
 
 template <bool FC1, int DT, int BITS, int KS, int P, bool RAW>
 hipError_t run(const ProjLaunch& p, const DecodePlan& plan, hipStream_t s)
@@ -506,6 +542,7 @@ hipError_t launch_stream(const ProjLaunch& p, const DecodePlan& plan, hipStream_
     }
     return raw ? launch_split<FC1, DT, 4, true>(p, plan, s) : launch_split<FC1, DT, 4, false>(p, plan, s);
 }
+
 
 }  // namespace
 
