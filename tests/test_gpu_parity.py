@@ -241,6 +241,19 @@ def test_layer_large_prefill_tile(dtype, bits, zp, bs, act):
     _layer_check(spec, 900 + bs, tokens=tokens)
 
 
+@pytest.mark.parametrize("dtype,bits,zp,bs", [(1, (4, 3), "sym", 64), (2, (2, 4), "u8", 128),
+                                           (1, (3, 2), "zpo", 16)])
+def test_layer_mid_prefill_tile(dtype, bits, zp, bs):
+    # 4096 routes against I = 1024: the 64-row prefill tile over many items,
+    # every zero-point mode, 16-input blocks included
+    spec = synth.custom(T=2048, H=256, I=1024, E=4, k=2, fc1_bits=bits[0], fc2_bits=bits[1],
+                        block_size=bs, dtype=dtype, act=dtype - 1, zp_mode=zp,
+                        zpo=1.5 if zp == "zpo" else math.nan, zp_range=(0, 3),
+                        name=f"mid_tile_{dtype}_{bits}_{zp}_{bs}")
+    tokens = np.unique(np.concatenate([np.linspace(0, 2047, 40).astype(np.int64), [3, 2044]]))
+    _layer_check(spec, 700 + bs, tokens=tokens)
+
+
 @pytest.mark.parametrize("T", [3, 70])
 def test_layer_block_size_16(T):
     # 16-input blocks: each 32-code span holds two blocks (decode T=3, prefill T=70)
