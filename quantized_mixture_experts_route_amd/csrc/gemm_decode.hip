@@ -342,6 +342,150 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(ProjLaunch p,
     }
 }
 
+// ---------------------------------------------------------------- row blocks
+// The m-tile list again, for many experts with few rows each (tiles of at
+// most MTR rows): every wavefront owns 16 weight rows of the tile's expert
+// over the whole of K, so its partial sums never leave it and nothing is
+// reduced across wavefronts.  The eight wavefronts of a workgroup (128
+// weight rows) share the tile's A rows and their rows' scale table in LDS.
+// A wavefront requests all of its code spans (one per 128-input super-step,
+// in the MFMA lane layout of mfma_chunk) right after the scale units and the
+// A rows, before it waits for anything, and consumes them in order, so the
+// first MFMAs start while later spans are still in flight.  fc1: columns
+// 0-7 of a wavefront are the gate rows and 8-15 the up rows of 8 activation
+// columns, paired in the epilogue by a DPP rotate.
+constexpr int kRowsWave = 16;
+constexpr int kRowsItem = kWaves * kRowsWave;  // weight rows per workgroup
+constexpr int kRowsScUnits = kRowsItem * (kChunkK / 32 / 8) / kThreads;  // 16-byte scale units per thread
+constexpr int kDppRotate8 = 0x128;  // DPP row_ror:8: lane c reads lane c ^ 8 of its row
+
+template <int DT, int BITS, bool FC1, int ZP, int MTR, int SS>
+__global__ __launch_bounds__(kThreads, 4) void decode_rows_kernel(ProjLaunch p,
+                                                                  const int32_t* __restrict__ tiles,
+                                                                  const int32_t* __restrict__ n_tiles_ptr)
+{
+    static_assert(ZP != kZpTensor, "scales only: a constant zero point");
+    static_assert(MTR == 8 || MTR == 16, "A rows are staged by one or two rounds of wavefronts");
+    constexpr Order O = code_order<DT, BITS>();
+    __shared__ __attribute__((aligned(16))) uint32_t lds[MTR * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t sc_tab[kRowsItem * kScPitch];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const int K = p.K;
+    const int nt = p.N / kRowsItem;
+    const int tile = blockIdx.x / nt;
+    const int n = blockIdx.x - tile * nt;
+    if (tile >= *n_tiles_ptr) return;  // whole workgroup
+    const int32_t* it = tiles + (int64_t)kDecodeTileInts * tile;
+    const int e = it[0];
+    const int row0 = it[1];
+    const int rows = it[2];
+    const int n_super = K / kSuperK;
+    const int n_blocks = K / p.block_size;
+    const int bs_shift = __builtin_ctz((unsigned)p.block_size);  // a power of two
+    const int64_t wbase = (int64_t)e * p.N + (int64_t)n * kRowsItem;  // the workgroup's first weight row
+    // MFMA column c: fc1 gate row 2c (c < 8) or up row 2(c-8)+1 of the
+    // wavefront's 8 activation columns; fc2 row c
+    const int trow = kRowsWave * wave + (FC1 ? 2 * (c & 7) + (c >> 3) : c);
+    const int row_bytes = K * BITS / 8;
+    const uint8_t* wcodes = p.w.codes + (wbase + trow) * row_bytes;
+    const uint16_t* a_src = reinterpret_cast<const uint16_t*>(p.a);
+    const int spans = K / 32;
+    const int sl = min(lane, spans - 1);
+    // fc2: route ids of MFMA rows 4g..4g+3 (entries past the tile's rows are 0)
+    int y2_row[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y2_row[i] = FC1 ? 0 : it[kDecodeTileRoutes + 4 * g + i];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 1) scale units: 8 blocks of one of the workgroup's rows each
+    const uint16_t* sc_src = reinterpret_cast<const uint16_t*>(p.w.scales) + wbase * n_blocks;
+    const int upr = n_blocks >> 3;
+    const int n_units = kRowsItem * upr;
+    u32x4 sc_unit[kRowsScUnits];
+#pragma unroll
+    for (int k = 0; k < kRowsScUnits; ++k) {
+        const int u = min(tid + kThreads * k, n_units - 1);
+        const int r = u / upr;
+        sc_unit[k] = *reinterpret_cast<const u32x4*>(sc_src + r * n_blocks + 8 * (u - r * upr));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2) A rows: tile row `wave` (and wave + 8), one 32-value span per lane
+    auto a_row_of = [&](int m) -> int64_t {
+        return FC1 ? it[kDecodeTileTokens + m] : row0 + min(m, rows - 1);
+    };
+    uint32_t a_stage[MTR / kWaves][16];
+#pragma unroll
+    for (int h = 0; h < MTR / kWaves; ++h) load_a_span(a_src + a_row_of(wave + kWaves * h) * K, 32 * sl, a_stage[h]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3) every code span of the wavefront (past K: the last one again, unused)
+    Span<BITS> sp[SS];
+#pragma unroll
+    for (int s = 0; s < SS; ++s) sp[s] = load_span<BITS>(wcodes, min(s, n_super - 1) * kSuperK + 32 * g);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 4) A rows and scales to LDS
+#pragma unroll
+    for (int h = 0; h < MTR / kWaves; ++h) {
+        const int m = wave + kWaves * h;
+        if (m < rows && lane < spans) store_a<O>(lds, m, lane, a_stage[h]);
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsScUnits; ++k) {
+        const int u = tid + kThreads * k;
+        if (u < n_units) {
+            const int r = u / upr;
+            uint32_t* dst = reinterpret_cast<uint32_t*>(sc_tab + r * kScPitch + 8 * (u - r * upr));
+            *reinterpret_cast<u32x2*>(dst) = u32x2{sc_unit[k].x, sc_unit[k].y};
+            *reinterpret_cast<u32x2*>(dst + 2) = u32x2{sc_unit[k].z, sc_unit[k].w};
+        }
+    }
+    __syncthreads();
+
+    // 5) the spans in order; two accumulator chains.  MFMA rows past the
+    //    tile's rows read a clamped LDS row and are never stored.
+    const uint32_t* a_lds = lds + min(c, MTR - 1) * kPitch;
+    const uint16_t* sc_row = sc_tab + trow * kScPitch;
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < SS; ++s) {
+        if (s < n_super) {  // uniform
+            const int kk = s * kSuperK + 32 * g;
+            BlockParams q;
+            q.zp = p.w.zp_fallback;
+            q.scale = Dt<DT>::to_float(sc_row[kk >> bs_shift]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(a_lds + kk / 2 + 4 * t);
+                acc[s & 1] = Dt<DT>::mfma(a, dequant_zp<DT, BITS, ZP>(sp[s], t, q), acc[s & 1]);
+            }
+        }
+    }
+    const f32x4 sum = acc[0] + acc[1];
+
+    // 6) epilogue: lane (g, c) holds MFMA rows 4g..4g+3 of column c
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = 4 * g + i;
+        if constexpr (FC1) {
+            const float up = dpp_f32<kDppRotate8>(sum[i]);  // column c + 8: the up row of column c
+            if (m < rows && c < 8) {
+                const int I = p.N / 2;
+                uint16_t* out = reinterpret_cast<uint16_t*>(p.act_out) + (int64_t)(row0 + m) * I;
+                out[n * (kRowsItem / 2) + 8 * wave + c] = Dt<DT>::from_float(act_value<DT>(p.act, sum[i], up));
+            }
+        } else {
+            if (m < rows) p.y2[(int64_t)y2_row[i] * p.N + n * kRowsItem + kRowsWave * wave + c] = sum[i];
+        }
+    }
+}
+
 // ---------------------------------------------------------------- expert-stationary
 // m-tiles of kExpertRows rows (one A row per wavefront), so the A rows, the
 // staged weights and the scale table share the LDS of two workgroups per CU.
@@ -574,6 +718,44 @@ hipError_t launch_zp(const ProjLaunch& p, const DecodePlan* plan, hipStream_t s)
     return launch_one<FC1, DT, NB, BITS, kZpGeneric, false>(p, plan, s);
 }
 
+template <bool FC1, int DT, int BITS, int ZP, int MTR>
+hipError_t launch_rows_ss(const ProjLaunch& p, hipStream_t s)
+{
+    const int n_super = p.K / kSuperK;
+    const dim3 grid((unsigned)(p.tiles_cap * (p.N / kRowsItem)));
+    if (n_super <= 4) {
+        launch(decode_rows_kernel<DT, BITS, FC1, ZP, MTR, 4>, grid, dim3(kThreads), s, p, p.worklist, p.n_items);
+    } else if (n_super <= 8) {
+        launch(decode_rows_kernel<DT, BITS, FC1, ZP, MTR, 8>, grid, dim3(kThreads), s, p, p.worklist, p.n_items);
+    } else {
+        launch(decode_rows_kernel<DT, BITS, FC1, ZP, MTR, 16>, grid, dim3(kThreads), s, p, p.worklist, p.n_items);
+    }
+    return hipGetLastError();
+}
+
+template <bool FC1, int DT, int BITS>
+hipError_t launch_rows_bits(const ProjLaunch& p, int max_rows, hipStream_t s)
+{
+    const bool generic = zp_mode(p.w) == kZpGeneric;
+    if (max_rows <= 8) {
+        return generic ? launch_rows_ss<FC1, DT, BITS, kZpGeneric, 8>(p, s)
+                       : launch_rows_ss<FC1, DT, BITS, kZpConst, 8>(p, s);
+    }
+    return generic ? launch_rows_ss<FC1, DT, BITS, kZpGeneric, 16>(p, s)
+                   : launch_rows_ss<FC1, DT, BITS, kZpConst, 16>(p, s);
+}
+
+template <bool FC1, int DT>
+hipError_t launch_rows_dt(const ProjLaunch& p, int max_rows, hipStream_t s)
+{
+    switch (p.w.bits) {
+    case 2: return launch_rows_bits<FC1, DT, 2>(p, max_rows, s);
+    case 3: return launch_rows_bits<FC1, DT, 3>(p, max_rows, s);
+    case 4: return launch_rows_bits<FC1, DT, 4>(p, max_rows, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <bool FC1, int DT, int NB>
 hipError_t launch_dt(const ProjLaunch& p, const DecodePlan* plan, hipStream_t s)
 {
@@ -595,6 +777,26 @@ hipError_t launch_fc1_decode(const ProjLaunch& p, const DecodePlan* plan, int dt
     }
     return dtype == kBF16 ? launch_dt<true, kBF16, kDecodeFc1Blocks>(p, plan, s)
                           : launch_dt<true, kF16, kDecodeFc1Blocks>(p, plan, s);
+}
+
+bool rows_fits(const ProjArgs& w, int K, int N, int block_size)
+{
+    const int bs = block_size;
+    return w.zp == nullptr && K % kSuperK == 0 && K <= kChunkK && N % kRowsItem == 0 && bs >= 32 &&
+           (bs & (bs - 1)) == 0 && (K / bs) % 8 == 0 && reinterpret_cast<uintptr_t>(w.scales) % 16 == 0;
+}
+
+hipError_t launch_rows_decode(const ProjLaunch& p, bool fc1, int max_rows, int dtype, hipStream_t s)
+{
+    if (!rows_fits(p.w, p.K, p.N, p.block_size) || max_rows < 1 || max_rows > kDecodeMT) {
+        return hipErrorInvalidValue;
+    }
+    if (fc1) {
+        return dtype == kBF16 ? launch_rows_dt<true, kBF16>(p, max_rows, s)
+                              : launch_rows_dt<true, kF16>(p, max_rows, s);
+    }
+    return dtype == kBF16 ? launch_rows_dt<false, kBF16>(p, max_rows, s)
+                          : launch_rows_dt<false, kF16>(p, max_rows, s);
 }
 
 hipError_t launch_fc2_decode(const ProjLaunch& p, const DecodePlan* plan, int dtype, hipStream_t s)

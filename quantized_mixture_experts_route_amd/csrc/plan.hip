@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(
     float* __restrict__ weights, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
     int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles)
 {
-    __shared__ int s_e[kDecodeMaxRoutes];      // expert of route r
+    __shared__ __attribute__((aligned(16))) int s_e[kDecodeMaxRoutes];  // expert of route r
     __shared__ int s_route[kDecodeMaxRoutes];  // route at sorted position p
     __shared__ int s_end[kDecodeMaxRoutes];    // end of position p's expert group
     __shared__ int s_tile_pos[kDecodeMaxRoutes];
@@ -41,6 +41,10 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(
     const int wave = tid >> 6;
     const int lane = tid & (kWave - 1);
     const int R = T * top_k;
+
+    // routes past R keep a sentinel above every expert, so the rank loop
+    // reads the whole table without a bound
+    if (tid >= R && tid < kDecodeMaxRoutes) s_e[tid] = INT32_MAX;
 
     // 1) routing
     for (int t = wave; t < T; t += kWaves) {
@@ -58,11 +62,17 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(
     if (tid < R) {
         const int e = s_e[tid];
         int less = 0, before = 0, same = 0;
-        for (int q = 0; q < R; ++q) {
-            const int f = s_e[q];
-            less += f < e;
-            same += f == e;
-            before += (f == e) & (q < tid);
+        const int4* tab = reinterpret_cast<const int4*>(s_e);
+#pragma unroll
+        for (int q4 = 0; q4 < kDecodeMaxRoutes / 4; ++q4) {  // 16-byte reads, all issued at once
+            const int4 f = tab[q4];
+            const int fs[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                less += fs[i] < e;
+                same += fs[i] == e;
+                before += (fs[i] == e) & (4 * q4 + i < tid);
+            }
         }
         const int pos = less + before;
         s_route[pos] = tid;
@@ -83,26 +93,18 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(
     if (start) s_tile_pos[rank] = tid;
     __syncthreads();
 
-    for (int idx = tid; idx < total * kDecodeTileInts; idx += kThreads) {
-        const int j = idx / kDecodeTileInts;
-        const int f = idx - j * kDecodeTileInts;
+    // one thread per (tile, row): the row's token and route ids, and rows 0..3
+    // write the tile's header
+    for (int u = tid; u < total * kDecodeMT; u += kThreads) {
+        const int j = u / kDecodeMT;
+        const int i = u - j * kDecodeMT;
         const int p0 = s_tile_pos[j];
         const int rows = min(kDecodeMT, s_end[p0] - p0);
-        int v = 0;
-        if (f == 0) {
-            v = s_e[s_route[p0]];
-        } else if (f == 1) {
-            v = p0;
-        } else if (f == 2) {
-            v = rows;
-        } else if (f >= 4) {
-            const int i = (f - 4) % kDecodeMT;
-            if (i < rows) {
-                const int r = s_route[p0 + i];
-                v = f < 4 + kDecodeMT ? r / top_k : r;
-            }
-        }
-        tiles[idx] = v;
+        const int r = s_route[p0 + min(i, rows - 1)];
+        int32_t* tile = tiles + (int64_t)j * kDecodeTileInts;
+        tile[kDecodeTileTokens + i] = i < rows ? r / top_k : 0;
+        tile[kDecodeTileRoutes + i] = i < rows ? r : 0;
+        if (i < 4) tile[i] = i == 0 ? s_e[s_route[p0]] : i == 1 ? p0 : i == 2 ? rows : 0;
     }
     if (tid == 0) *n_tiles = total;
 }

@@ -98,6 +98,7 @@ struct Layout {
     int m_tile;
     int nt1, nt2;       // n-tiles of fc1 (activation columns) and fc2 (hidden columns)
     int64_t cap1, cap2;  // work-list capacities
+    int64_t m_tiles;     // m-tile capacity
     size_t ids, w, offsets, sorted, wl1, n1, wl2, n2, act, y2, total;
 };
 
@@ -120,6 +121,7 @@ bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L,
     L->nt1 = (int)ceil_div(I, fc1_cols);
     L->nt2 = (int)ceil_div(H, fc2_cols);
     const int64_t m_tiles = ceil_div(R, L->m_tile) + (E < R ? E : R);
+    L->m_tiles = m_tiles;
     if (!mul_ok(m_tiles, L->nt1, &L->cap1) || !mul_ok(m_tiles, L->nt2, &L->cap2) ||
         L->cap1 > INT32_MAX || L->cap2 > INT32_MAX) {
         return false;
@@ -369,6 +371,12 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
                              I <= 2048 && fc1->bits == 2 && fc1->zero_points == nullptr;
     qmoe::DecodePlan plan{logits, (int)T, E, normalize, w, topk_ids_out, topk_w_out, offsets, sorted};
     const qmoe::DecodePlan* dplan = expert_mode ? &plan : nullptr;
+    // Row-block kernels for the m-tile list: an expert has at most one route
+    // per token, so a tile holds at most min(T, 16) rows.
+    const bool list_mode = L.decode && !expert_mode && !stream_mode;
+    const int max_rows = (int)(T < qmoe::kDecodeMT ? T : qmoe::kDecodeMT);
+    const bool rows1 = list_mode && qmoe::rows_fits(w1, H, 2 * I, block_size);
+    const bool rows2 = list_mode && qmoe::rows_fits(w2, I, H, block_size);
     if (L.decode && !expert_mode && !stream_mode) {  // routing, grouping and the m-tile list in one launch
         timer_begin(QMOE_STAGE_ROUTE, s);
         e = qmoe::launch_decode_plan(logits, (int)T, E, top_k, normalize, w, topk_ids_out,
@@ -401,10 +409,12 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     p1.worklist = wl1;
     p1.n_items = n1;
     p1.grid = L.cap1 > 0 ? L.cap1 : 1;
+    p1.tiles_cap = L.m_tiles;
     p1.act = activation;
     p1.act_out = act;
     timer_begin(QMOE_STAGE_FC1, s);
     e = stream_mode ? qmoe::launch_fc1_stream(p1, plan, dtype, s)
+        : rows1     ? qmoe::launch_rows_decode(p1, true, max_rows, dtype, s)
         : L.decode  ? qmoe::launch_fc1_decode(p1, dplan, dtype, s)
                     : qmoe::launch_fc1_prefill(p1, dtype, s);
     timer_end(QMOE_STAGE_FC1, s);
@@ -423,9 +433,11 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     p2.worklist = wl2;
     p2.n_items = n2;
     p2.grid = L.cap2 > 0 ? L.cap2 : 1;
+    p2.tiles_cap = L.m_tiles;
     p2.y2 = y2;
     timer_begin(QMOE_STAGE_FC2, s);
     e = stream_mode ? qmoe::launch_fc2_stream(p2, plan, dtype, s)
+        : rows2     ? qmoe::launch_rows_decode(p2, false, max_rows, dtype, s)
         : L.decode  ? qmoe::launch_fc2_decode(p2, dplan, dtype, s)
                     : qmoe::launch_fc2_prefill(p2, dtype, s);
     timer_end(QMOE_STAGE_FC2, s);

@@ -81,6 +81,7 @@ struct ProjLaunch {
     const int32_t* worklist;  // prefill: [cap, 3] triples; decode: m-tiles
     const int32_t* n_items;   // prefill: [1] items; decode: [1] m-tiles
     int64_t grid;             // decode: workgroups to launch; prefill: item bound
+    int64_t tiles_cap;        // decode: capacity of the m-tile list
     int act;                  // fc1 only
     void* act_out;            // fc1: dtype [R, I] in sorted order
     float* y2;                // fc2: float32 [R, H] by route id
@@ -119,6 +120,12 @@ hipError_t launch_fc2_prefill(const ProjLaunch& p, int dtype, hipStream_t s);
 // the expert-stationary kernels (K <= 2048, E <= 64, R <= kDecodeMaxRoutes).
 hipError_t launch_fc1_decode(const ProjLaunch& p, const DecodePlan* plan, int dtype, hipStream_t s);
 hipError_t launch_fc2_decode(const ProjLaunch& p, const DecodePlan* plan, int dtype, hipStream_t s);
+
+// Row-block decode projections over the m-tile list (tiles of at most
+// max_rows <= 16 rows; a constant zero point, K <= 2048, 128 weight rows per
+// workgroup).  rows_fits: the projection's shapes and scales suit the kernel.
+bool rows_fits(const ProjArgs& w, int K, int N, int block_size);
+hipError_t launch_rows_decode(const ProjLaunch& p, bool fc1, int max_rows, int dtype, hipStream_t s);
 
 // Streamed decode projections (R = T*top_k <= 16, E <= 64): every expert's
 // weights requested at launch and consumed piece by piece as they land; fc1

@@ -31,12 +31,19 @@ __device__ inline float key_to_logit(int32_t key)
 }
 
 // Routes one token; the whole wavefront calls it.  get(j) returns this lane's
-// logit of expert lane + 64 j (called only for experts < E).  For every slot
-// s < top_k exactly one lane calls emit(s, expert, weight).
+// logit of expert lane + 64 j; it is called once for every j < EPL, also where
+// lane + 64 j >= E (the value is then ignored), so that all of a lane's loads
+// are issued before the first one is waited on.  For every slot s < top_k
+// exactly one lane calls emit(s, expert, weight).
 template <int EPL, class Get, class Emit>
 __device__ inline void route_values(int E, int top_k, int normalize, Get get, Emit emit)
 {
     const int lane = threadIdx.x & (kWave - 1);
+    float val[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+        val[j] = get(j);
+    }
     uint64_t cand[EPL];
     float m = -INFINITY;
 #pragma unroll
@@ -44,7 +51,7 @@ __device__ inline void route_values(int E, int top_k, int normalize, Get get, Em
         const int e = lane + kWave * j;
         cand[j] = 0;
         if (e < E) {
-            const float v = get(j);
+            const float v = val[j];
             const uint32_t ukey = (uint32_t)route_key(v) ^ 0x80000000u;
             cand[j] = ((uint64_t)ukey << 32) | (uint32_t)~(uint32_t)e;
             if (v > m) {
@@ -87,7 +94,7 @@ __device__ inline void route_values(int E, int top_k, int normalize, Get get, Em
         for (int j = 0; j < EPL; ++j) {
             const int e = lane + kWave * j;
             if (e < E) {
-                part += expf(get(j) - m);
+                part += expf(val[j] - m);
             }
         }
         den = wave_sum_f32(part);
@@ -106,7 +113,7 @@ template <int EPL, class Emit>
 __device__ inline void route_token(const float* row, int E, int top_k, int normalize, Emit emit)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    route_values<EPL>(E, top_k, normalize, [&](int j) { return row[lane + kWave * j]; }, emit);
+    route_values<EPL>(E, top_k, normalize, [&](int j) { return row[min(lane + kWave * j, E - 1)]; }, emit);
 }
 
 }  // namespace qmoe

@@ -317,6 +317,45 @@ def test_layer_stream_decode_one_expert_sixteen_rows():
     _layer_check(spec, 1350, logits=logits)
 
 
+# Row-block decode over the m-tile list (more experts than routes, or widths
+# the streamed kernels do not take): every wavefront owns 16 weight rows over
+# all of K.  Cases cover the 8- and 16-row A tiles (T <= 8 and T > 8), one,
+# two and four K super-steps past the last real one (K = 256, 1280, 768 in
+# 4-, 16- and 8-span variants), all three widths on both projections, both
+# dtypes and activations, a fractional and a generic zero-point offset, and
+# two scale units per thread (64 blocks per row).
+ROWS = [
+    dict(T=12, H=1024, I=1024, E=96, k=6, fc1_bits=4, fc2_bits=3, block_size=64, dtype=1, act=1,
+         zp_mode="sym", zpo=math.nan),
+    dict(T=5, H=1280, I=512, E=40, k=4, fc1_bits=4, fc2_bits=2, block_size=32, dtype=1, act=0,
+         zp_mode="zpo", zpo=0.75),
+    dict(T=3, H=256, I=256, E=16, k=3, fc1_bits=2, fc2_bits=3, block_size=32, dtype=1, act=1,
+         zp_mode="sym", zpo=math.nan),
+    dict(T=7, H=2048, I=768, E=100, k=8, fc1_bits=3, fc2_bits=4, block_size=32, dtype=2, act=0,
+         zp_mode="zpo", zpo=1.5),
+    dict(T=10, H=768, I=1024, E=200, k=8, fc1_bits=2, fc2_bits=2, block_size=32, dtype=2, act=1,
+         zp_mode="sym", zpo=math.nan),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ROWS)))
+def test_layer_rows_decode(case):
+    spec = synth.custom(name=f"rows{case}", **ROWS[case])
+    _layer_check(spec, 1400 + case)
+
+
+@pytest.mark.parametrize("T,E,k,fc1_bits", [(16, 4, 1, 3), (8, 70, 2, 4)])
+def test_layer_rows_decode_full_tile(T, E, k, fc1_bits):
+    # every token's first choice is expert 1: one tile of T rows (16 and 8,
+    # the two A tile heights), the other routes on tiles of their own
+    spec = synth.custom(T=T, H=512, I=512, E=E, k=k, fc1_bits=fc1_bits, fc2_bits=4, block_size=32,
+                        dtype=2, act=0, zp_mode="zpo", zpo=1.5, name=f"rows_full{T}")
+    rng = np.random.default_rng(1450 + T)
+    logits = rng.normal(0.0, 1.0, size=(T, E)).astype(np.float32)
+    logits[:, 1] = 8.0
+    _layer_check(spec, 1450 + T, logits=logits)
+
+
 @pytest.mark.parametrize("T", [5, 300])
 def test_layer_all_tokens_one_expert(T):
     spec = synth.custom(T=T, H=256, I=256, E=8, k=1, fc1_bits=3, fc2_bits=4, block_size=32,
