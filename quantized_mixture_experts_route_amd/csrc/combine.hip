@@ -3,7 +3,8 @@
 // [qmoe.rs, qmoe_combine]: out[t, h] = sum over slots s = 0..k-1, in slot
 // order, of w[t, s] * y2[t*k + s, h], accumulated in float32 and rounded once
 // to the output dtype.  Each thread owns four consecutive h of one token, so
-// there are no atomics and the result is deterministic.
+// there are no atomics and the result is deterministic.  When fc2 split its
+// K range, each y2 row is first summed over its parts, in part order.
 #include "qmoe_device.h"
 #include "qmoe_internal.h"
 
@@ -11,7 +12,8 @@ namespace qmoe {
 namespace {
 
 template <int DT>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y2,
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y2, int parts,
+                                                      int64_t part_stride,
                                                       const float* __restrict__ w, int64_t T,
                                                       int H, int top_k,
                                                       uint16_t* __restrict__ out)
@@ -25,7 +27,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     for (int s = 0; s < top_k; ++s) {
         const int64_t r = t * top_k + s;
         const float wt = w[r];
-        const float4 v = *reinterpret_cast<const float4*>(y2 + r * H + h);
+        float4 v = *reinterpret_cast<const float4*>(y2 + r * H + h);
+        for (int q = 1; q < parts; ++q) {
+            const float4 u = *reinterpret_cast<const float4*>(y2 + q * part_stride + r * H + h);
+            v.x += u.x;
+            v.y += u.y;
+            v.z += u.z;
+            v.w += u.w;
+        }
         sum.x += wt * v.x;
         sum.y += wt * v.y;
         sum.z += wt * v.z;
@@ -39,16 +48,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const float* y2, const float* weights, int64_t T, int H, int top_k,
-                          void* out, int dtype, hipStream_t s)
+hipError_t launch_combine(const float* y2, int parts, int64_t part_stride, const float* weights,
+                          int64_t T, int H, int top_k, void* out, int dtype, hipStream_t s)
 {
     const int64_t n = T * (H / 4);
     const dim3 grid((unsigned)((n + 255) / 256)), block(256);
     uint16_t* o = reinterpret_cast<uint16_t*>(out);
     if (dtype == kBF16) {
-        launch(combine_kernel<kBF16>, grid, block, s, y2, weights, T, H, top_k, o);
+        launch(combine_kernel<kBF16>, grid, block, s, y2, parts, part_stride, weights, T, H, top_k, o);
     } else {
-        launch(combine_kernel<kF16>, grid, block, s, y2, weights, T, H, top_k, o);
+        launch(combine_kernel<kF16>, grid, block, s, y2, parts, part_stride, weights, T, H, top_k, o);
     }
     return hipGetLastError();
 }

@@ -66,25 +66,35 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
     const int g = lane >> 4;
     const int c = lane & 15;
     const int K = p.K;
-    const int n_super = K / kSuperK;
     const int n_items = *p.n_items;
+    // fc2 may split K into p.k_split equal parts, each a work-list column of
+    // its own (n-tile index ks * nt + n) writing float32 partial sums to part
+    // ks of y2; the combine adds the parts in order
+    const int k_split = FC1 ? 1 : p.k_split;
+    const int n_super = K / kSuperK / k_split;  // super-steps per item
     const uint16_t* a_src = reinterpret_cast<const uint16_t*>(p.a);
     const uint32_t row_bytes = (uint32_t)K * BITS / 8;
     const uint32_t n_blocks = (uint32_t)(K / p.block_size);
     const uint32_t zp_bytes = BITS == 3 ? n_blocks : (n_blocks + 8 / BITS - 1) / (8 / BITS);
     const int bs_shift = __builtin_ctz((unsigned)p.block_size);  // block_size is a power of two
     const int nt = FC1 ? (p.N / 2 + kRows / 2 - 1) / (kRows / 2) : (p.N + kRows - 1) / kRows;
+    const int ss_shift = bs_shift - 4;  // super-steps per scale stage: block_size / 16
     const int G = gridDim.x;  // a multiple of kXcds
     const int vb = (int)(blockIdx.x % kXcds) * (G / kXcds) + (int)(blockIdx.x / kXcds);
 
     for (int item = vb; item < n_items; item += G) {
         const int e = p.worklist[3 * item + 0];
-        const int local0 = p.worklist[3 * item + 1] * nt + p.worklist[3 * item + 2];
+        // the work-list's column index runs over nt * k_split (fc2: the K part, then the n-tile)
+        const int local0 = p.worklist[3 * item + 1] * (nt * k_split) + p.worklist[3 * item + 2];
         const int first = p.offsets[e];
         const int count = p.offsets[e + 1] - first;
         const int mt_e = (count + MT - 1) / MT;
         const int mt = local0 % mt_e;  // m inner
-        const int ntile = local0 / mt_e;
+        const int ntk = local0 / mt_e;
+        const int ks = ntk / nt;        // K part
+        const int ntile = ntk - ks * nt;
+        const int s_begin = ks * n_super;  // first super-step of the part
+        const int s_end = s_begin + n_super;
         const int row0 = first + mt * MT;
         const int rows = min(MT, count - mt * MT);
 
@@ -120,8 +130,7 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
         const uint32_t wr_base = active ? (FC1 ? 2 * col0 : col0) : 0;
         const uint16_t* sc_row = scales_e + (wr_base + lane) * n_blocks;
         const int sc_slot_store = FC1 ? ((lane >> 1) | ((lane & 1) << 5)) : lane;
-        const int ss_shift = bs_shift - 4;  // super-steps per stage: block_size / 16
-        const int n_stages = (int)(n_blocks >> 3);
+        const int stage_end = s_end >> ss_shift;  // parts hold whole stages
         u32x4 sc_next;
         auto stage_load = [&](int stage) { sc_next = *reinterpret_cast<const u32x4*>(sc_row + 8 * stage); };
 
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
                 if ((s & ((1 << ss_shift) - 1)) == 0) {  // first super-step of a stage
                     *reinterpret_cast<u32x4*>(&sc_lds[wave][sc_slot_store * 8]) = sc_next;
                     const int next = (s >> ss_shift) + 1;
-                    if (next < n_stages) stage_load(next);
+                    if (next < stage_end) stage_load(next);
                 }
             }
 #pragma unroll
@@ -226,10 +235,10 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
 
         Span<BITS> sp[4];
         RawParams bp[4];
-        if constexpr (STAGED) stage_load(0);
-        load_a(0);
-        load_b(0, sp, bp);
-        for (int s = 0; s < n_super; ++s) {
+        if constexpr (STAGED) stage_load(s_begin >> ss_shift);
+        load_a(s_begin);
+        load_b(s_begin, sp, bp);
+        for (int s = s_begin; s < s_end; ++s) {
             uint32_t* buf = a_lds[s & 1];
             store_a(buf);
             Span<BITS> cur[4];
@@ -240,7 +249,7 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
                 cbp[nb] = bp[nb];
             }
             __syncthreads();
-            if (s + 1 < n_super) {  // in flight during the MFMAs below
+            if (s + 1 < s_end) {  // in flight during the MFMAs below
                 load_a(s + 1);
                 load_b(s + 1, sp, bp);
             }
@@ -261,7 +270,7 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
                     out[col0 + 16 + c] =
                         Dt<DT>::from_float(act_value<DT>(p.act, acc[mb][2][i], acc[mb][3][i]));
                 } else {
-                    float* out = p.y2 + (int64_t)row_dst[m] * p.N;
+                    float* out = p.y2 + ks * p.part_stride + (int64_t)row_dst[m] * p.N;
 #pragma unroll
                     for (int nb = 0; nb < 4; ++nb) out[col0 + nb * 16 + c] = acc[mb][nb][i];
                 }
@@ -298,11 +307,12 @@ int64_t persistent_grid(Kernel kernel, int threads, int64_t item_bound)
     return (g + kXcds - 1) / kXcds * kXcds;
 }
 
-// Scales can be staged eight blocks at a time when a row holds whole stages
-// and the 16-byte loads are aligned.
-inline bool can_stage(const ProjLaunch& p)
+// Scales can be staged eight blocks at a time when every K part of a row
+// holds whole stages and the 16-byte loads are aligned.
+inline bool can_stage(const ProjLaunch& p, bool fc1)
 {
-    return p.block_size >= 32 && (p.K / p.block_size) % 8 == 0 &&
+    const int parts = fc1 ? 1 : p.k_split;
+    return p.block_size >= 32 && (p.K / parts / p.block_size) % 8 == 0 &&
            reinterpret_cast<uintptr_t>(p.w.scales) % 16 == 0;
 }
 
@@ -317,7 +327,8 @@ hipError_t run(Kernel kernel, const ProjLaunch& p, int threads, hipStream_t s)
 template <bool FC1, int DT, int BITS, int MT, int ZP>
 hipError_t launch_one(const ProjLaunch& p, hipStream_t s)
 {
-    if (can_stage(p)) return run(prefill_kernel<DT, BITS, FC1, MT, ZP, false, true>, p, MT * 4, s);
+    if (!FC1 && (p.k_split < 1 || p.K % (p.k_split * kSuperK))) return hipErrorInvalidValue;
+    if (can_stage(p, FC1)) return run(prefill_kernel<DT, BITS, FC1, MT, ZP, false, true>, p, MT * 4, s);
     if constexpr (MT == kPrefillMTSmall) {
         if (p.block_size < 32) return run(prefill_kernel<DT, BITS, FC1, MT, ZP, true, false>, p, MT * 4, s);
         return run(prefill_kernel<DT, BITS, FC1, MT, ZP, false, false>, p, MT * 4, s);

@@ -96,6 +96,7 @@ constexpr size_t kAlign = 256;
 struct Layout {
     bool decode;
     int m_tile;
+    int k_split_cap;    // prefill fc2: most K parts y2 and the fc2 work-list have room for
     int nt1, nt2;       // n-tiles of fc1 (activation columns) and fc2 (hidden columns)
     int64_t cap1, cap2;  // work-list capacities
     int64_t m_tiles;     // m-tile capacity
@@ -103,6 +104,33 @@ struct Layout {
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Prefill fc2 K split.  A work-list item of fc2 runs all of K = I, and the
+// persistent grid holds one item per workgroup slot, so a layer whose items
+// fill the last round poorly (or leave slots idle) finishes sooner with K cut
+// into S parts: S times the items, each 1/S as long.  The estimate counts
+// each expert's last m-tile as half full and assumes the 256 compute units of
+// the target GPU; S = 2 or 4 is taken only when it cuts the estimated
+// makespan (in full-K item times) by more than a tenth.  The choice depends on
+// shapes only, so the workspace size does too.
+int fc2_split(int64_t R, int E, int H, int I, int mt)
+{
+    constexpr int64_t kCUs = 256;
+    const int64_t nt = ceil_div(H, qmoe::prefill_fc2_cols(mt));
+    const int64_t items = (ceil_div(R, mt) + (E < R ? E : R) / 2) * nt;
+    const int64_t slots = kCUs * (mt == qmoe::kPrefillMTLarge ? 1 : 2);
+    int best = 1;
+    double best_cost = (double)ceil_div(items, slots);
+    for (int S = 2; S <= 4; S *= 2) {
+        if (I % (S * qmoe::kSuperK)) continue;
+        const double cost = (double)ceil_div(items * S, slots) / S;
+        if (cost < 0.9 * best_cost) {
+            best = S;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
 
 // prefill_mt: the prefill tile rows to lay the work-lists out for; the small
 // tile (the default) yields the most items, so its layout bounds the others.
@@ -116,18 +144,23 @@ bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L,
     }
     L->decode = R <= QMOE_DECODE_MAX_ROUTES;
     L->m_tile = L->decode ? qmoe::kDecodeMT : prefill_mt;
+    {
+        const int a = fc2_split(R, E, H, I, qmoe::kPrefillMTSmall);
+        const int b = fc2_split(R, E, H, I, qmoe::kPrefillMTLarge);
+        L->k_split_cap = L->decode ? 1 : (a > b ? a : b);
+    }
     const int fc1_cols = L->decode ? qmoe::kDecodeFc1Cols : qmoe::prefill_fc1_cols(L->m_tile);
     const int fc2_cols = L->decode ? qmoe::kDecodeFc2Cols : qmoe::prefill_fc2_cols(L->m_tile);
     L->nt1 = (int)ceil_div(I, fc1_cols);
     L->nt2 = (int)ceil_div(H, fc2_cols);
     const int64_t m_tiles = ceil_div(R, L->m_tile) + (E < R ? E : R);
     L->m_tiles = m_tiles;
-    if (!mul_ok(m_tiles, L->nt1, &L->cap1) || !mul_ok(m_tiles, L->nt2, &L->cap2) ||
+    if (!mul_ok(m_tiles, L->nt1, &L->cap1) || !mul_ok(m_tiles, (int64_t)L->nt2 * L->k_split_cap, &L->cap2) ||
         L->cap1 > INT32_MAX || L->cap2 > INT32_MAX) {
         return false;
     }
     int64_t act_bytes, y2_bytes;
-    if (!mul_ok(R, (int64_t)I * 2, &act_bytes) || !mul_ok(R, (int64_t)H * 4, &y2_bytes)) {
+    if (!mul_ok(R, (int64_t)I * 2, &act_bytes) || !mul_ok(R, (int64_t)H * 4 * L->k_split_cap, &y2_bytes)) {
         return false;
     }
     // the projection kernels address hidden [T, H] and act [R, I] with 32-bit element offsets
@@ -342,6 +375,15 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     }
 
     const int64_t R = T * top_k;
+    // fc2 K parts: the shape policy's choice for this tile, halved until each
+    // part holds whole super-steps and (for the large tile, which always
+    // stages its scales) whole 8-block scale stages
+    int k_split = L.decode ? 1 : fc2_split(R, E, H, I, L.m_tile);
+    while (k_split > 1 && (I % (k_split * qmoe::kSuperK) ||
+                           (L.m_tile == qmoe::kPrefillMTLarge && (I / k_split / block_size) % 8))) {
+        k_split /= 2;
+    }
+    if (k_split > L.k_split_cap) k_split = L.k_split_cap;
     char* ws = static_cast<char*>(workspace);
     int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
     float* w = reinterpret_cast<float*>(ws + L.w);
@@ -391,7 +433,7 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
 
         timer_begin(QMOE_STAGE_GROUP, s);
         e = qmoe::launch_group(ids, (int)R, E, L.m_tile, L.nt1, offsets, sorted, wl1, L.cap1, n1,
-                               L.nt2, wl2, L.cap2, n2, s);
+                               L.nt2 * k_split, wl2, L.cap2, n2, s);
         timer_end(QMOE_STAGE_GROUP, s);
         if (e != hipSuccess) return hip_fail(e, "group launch");
     }
@@ -435,6 +477,8 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     p2.grid = L.cap2 > 0 ? L.cap2 : 1;
     p2.tiles_cap = L.m_tiles;
     p2.y2 = y2;
+    p2.k_split = k_split;
+    p2.part_stride = R * (int64_t)H;
     timer_begin(QMOE_STAGE_FC2, s);
     e = stream_mode ? qmoe::launch_fc2_stream(p2, plan, dtype, s)
         : rows2     ? qmoe::launch_rows_decode(p2, false, max_rows, dtype, s)
@@ -444,7 +488,7 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     if (e != hipSuccess) return hip_fail(e, "fc2 launch");
 
     timer_begin(QMOE_STAGE_COMBINE, s);
-    e = qmoe::launch_combine(y2, w, T, H, top_k, out, dtype, s);
+    e = qmoe::launch_combine(y2, k_split, R * (int64_t)H, w, T, H, top_k, out, dtype, s);
     timer_end(QMOE_STAGE_COMBINE, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
 

@@ -84,7 +84,9 @@ struct ProjLaunch {
     int64_t tiles_cap;        // decode: capacity of the m-tile list
     int act;                  // fc1 only
     void* act_out;            // fc1: dtype [R, I] in sorted order
-    float* y2;                // fc2: float32 [R, H] by route id
+    float* y2;                // fc2: float32 [R, H] by route id (k_split parts)
+    int k_split;              // prefill fc2: K parts (1, 2 or 4), each a work-list column block
+    int64_t part_stride;      // prefill fc2: floats between the parts of y2
 };
 
 // Routing inputs and outputs of the expert-stationary decode kernels: fc1
@@ -135,8 +137,10 @@ bool stream_fits(const ProjArgs& w, int K, int N, int block_size, bool fc1);
 hipError_t launch_fc1_stream(const ProjLaunch& p, const DecodePlan& plan, int dtype, hipStream_t s);
 hipError_t launch_fc2_stream(const ProjLaunch& p, const DecodePlan& plan, int dtype, hipStream_t s);
 
-hipError_t launch_combine(const float* y2, const float* weights, int64_t T, int H, int top_k,
-                          void* out, int dtype, hipStream_t s);
+// y2 holds `parts` partial sums of the fc2 rows, part_stride floats apart;
+// they are added in part order before the routing weights apply.
+hipError_t launch_combine(const float* y2, int parts, int64_t part_stride, const float* weights,
+                          int64_t T, int H, int top_k, void* out, int dtype, hipStream_t s);
 
 hipError_t launch_dequant(const ProjArgs& w, int64_t rows, int K, int block_size, int dtype,
                           int32_t* codes_out, void* w_out, hipStream_t s);
