@@ -248,11 +248,11 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
                 cur[nb] = sp[nb];
                 cbp[nb] = bp[nb];
             }
-            __syncthreads();
-            if (s + 1 < s_end) {  // in flight during the MFMAs below
+            if (s + 1 < s_end) {  // in flight during the barrier and the MFMAs below
                 load_a(s + 1);
                 load_b(s + 1, sp, bp);
             }
+            __syncthreads();
             compute(buf, cur, cbp, s);
         }
 
