@@ -167,7 +167,10 @@ size_t qmoe_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t t
  * T = 0 returns QMOE_OK and enqueues nothing.
  * Numerics: dequantized weights are rounded to dtype (round to nearest even)
  * before the products, products accumulate in float32, the activation is
- * rounded to dtype, fc2 outputs stay float32 until the combine.
+ * rounded to dtype, fc2 outputs stay float32 until the combine.  For many
+ * routes, fc2 may split its K range into 2 or 4 parts (chosen from the sizes
+ * alone); their float32 partial sums are added in part order before the
+ * routing weights apply, so results stay deterministic.
  */
 int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, int32_t I,
                  int32_t E, const qmoe_proj* fc1, const qmoe_proj* fc2, float zero_point_offset,
