@@ -66,6 +66,8 @@ def _args():
                     help="print the digest of the kernel sources that traffic counters are tied to")
     ap.add_argument("--pmc-summary", metavar="DIR",
                     help="summarize rocprofv3 CSV files under DIR and exit")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the layer replayed from HIP graphs (one per weight copy)")
     ap.add_argument("--stages", action="store_true",
                     help="also time every stage separately after the timed region")
     return ap.parse_args()
@@ -267,6 +269,32 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
     }
+
+    if a.graph:
+        # one captured layer per weight copy, replayed in the same rotation
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[(warmup + i) % copies].replay()
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - t0) * 1e3 / steps
+        result["graph_replay"] = {"ms_per_step": round(g_ms, 5),
+                                  "tokens_per_s": round(T / (g_ms * 1e-3), 2)}
+        del graphs
 
     if a.stages:
         stage_ms = {}

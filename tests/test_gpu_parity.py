@@ -408,3 +408,33 @@ def test_layer_deterministic(cfg):
     c = dv.run_layer(dev, spec)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_layer_graph_replay(cfg):
+    # the whole layer captured in one HIP graph (its launches hold no memset
+    # and allocate nothing when out and workspace are given): every replay,
+    # with eager work and a synchronization in between, equals the eager call
+    spec = synth.workload(cfg)
+    inp = synth.make_inputs(spec, synth.seed_for(cfg))
+    dev = dv.to_device(inp, spec)
+    ws = qm.alloc_workspace(spec["T"], spec["H"], spec["I"], spec["E"], spec["k"],
+                            qm.dtype_code(dev["hidden"].dtype), dev["hidden"].device)
+    eager = dv.run_layer(dev, spec, workspace=ws).clone()
+    out = torch.empty_like(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a side stream before capture
+        dv.run_layer(dev, spec, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dv.run_layer(dev, spec, out=out, workspace=ws)
+    for _ in range(3):
+        out.zero_()
+        dv.run_layer(dev, spec, workspace=ws)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
