@@ -3,10 +3,11 @@
 //
 // [PR 33569: the decode path serves small expanded-row counts, and its time
 // is set by the packed-weight bytes; qmoe.rs QMoEKernel::execute: route,
-// group, fc1 + activation, fc2, combine.]  With R = T*top_k <= 16 every
-// selected expert's weights are read once and multiplied with at most 16
-// rows, so a projection costs the time to stream its bytes plus the work left
-// once the last of them arrives.  One workgroup of eight wavefronts per
+// group, fc1 + activation, fc2, combine.]  With at most 16 tokens (and
+// R = T*top_k <= 64 routes) every selected expert's weights are read once and
+// multiplied with at most 16 rows (a token routes to an expert at most once),
+// so a projection costs the time to stream its bytes plus the work left once
+// the last of them arrives.  One workgroup of eight wavefronts per
 // (expert, block of weight rows); wavefront w owns one block of 16 contiguous
 // weight rows and a 1/KS share of K.  fc1 (KS = 1): 128 rows per workgroup,
 // the 16 rows of a wavefront are 8 gate/up pairs, gate in MFMA columns 0-7
@@ -66,6 +67,7 @@ constexpr int kMaxBlocks = 64;               // quantization blocks per row (K /
 constexpr int kScPitch = kMaxBlocks + 4;     // scale table row pitch in uint16 (rows 8-byte aligned)
 constexpr int kScUnits = 2;                  // 16-byte scale units per thread at most (128 rows x 8)
 constexpr int kTokW = kRowsA / kWavesS;      // tokens each wavefront routes (T <= 16)
+constexpr int kMaxRoutesS = kWave;           // routes (T * top_k), one per lane of wavefront 0
 constexpr int kDppRor8 = 0x128;              // DPP row_ror:8: lane c reads lane c ^ 8 of its row
 
 // A kernel argument held in SGPRs from here on: the compiler may otherwise
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
     __shared__ float a_sum[kRowsA][kMaxSuper];  // RAW: -sum (b_r + zp) a of A row m over super-step s
     __shared__ __attribute__((aligned(16))) float m_sum[kMaxSuper][kRowsA];  // RAW: the same by MFMA row
     __shared__ __attribute__((aligned(16))) float red[KS == 2 ? kBlocksWG * kWave * 4 : 4];
-    __shared__ int s_e[kRowsA];     // fc1: expert of route r
+    __shared__ int s_e[kMaxRoutesS];  // fc1: expert of route r
     __shared__ int s_arow[kRowsA];  // fc1: A tile row (token) of the expert's m-th route
     __shared__ int s_info[2];       // fc1: first sorted position, route count
 
@@ -558,13 +560,14 @@ bool stream_fits(const ProjArgs& w, int K, int N, int block_size, bool fc1)
 
 hipError_t launch_fc1_stream(const ProjLaunch& p, const DecodePlan& plan, int dtype, hipStream_t s)
 {
-    if (plan.T > kRowsA || plan.T * p.top_k > kRowsA || plan.E > kWave) return hipErrorInvalidValue;
+    if (plan.T > kRowsA || plan.T * p.top_k > kMaxRoutesS || plan.E > kWave) return hipErrorInvalidValue;
     return dtype == kBF16 ? launch_stream<true, kBF16>(p, plan, s) : launch_stream<true, kF16>(p, plan, s);
 }
 
 hipError_t launch_fc2_stream(const ProjLaunch& p, const DecodePlan& plan, int dtype, hipStream_t s)
 {
-    if (plan.T * p.top_k > kRowsA) return hipErrorInvalidValue;
+    // an expert holds at most one route per token, so at most T rows
+    if (plan.T > kRowsA) return hipErrorInvalidValue;
     return dtype == kBF16 ? launch_stream<false, kBF16>(p, plan, s) : launch_stream<false, kF16>(p, plan, s);
 }
 

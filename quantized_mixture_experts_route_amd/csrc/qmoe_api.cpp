@@ -403,10 +403,10 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     // Chosen when every expert is likely selected, K fits one chunk and fc1's
     // block of weights fits the kernel's LDS staging (2-bit codes, no
     // zero-point tensor: the other variants run out of registers).
-    // Streamed decode (at most 16 expanded rows): the same idea with every
+    // Streamed decode (at most 16 tokens and 64 routes): the same idea with every
     // wavefront owning whole weight rows and consuming its weights piece by
     // piece as they arrive.
-    const bool stream_mode = L.decode && R <= 16 && E <= 64 && E <= R &&
+    const bool stream_mode = L.decode && T <= 16 && R <= 64 && E <= 64 && E <= R &&
                              qmoe::stream_fits(w1, H, 2 * I, block_size, true) &&
                              qmoe::stream_fits(w2, I, H, block_size, false);
     const bool expert_mode = !stream_mode && L.decode && E <= 64 && E <= R && H <= 2048 &&

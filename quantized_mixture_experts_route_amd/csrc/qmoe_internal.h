@@ -129,7 +129,7 @@ hipError_t launch_fc2_decode(const ProjLaunch& p, const DecodePlan* plan, int dt
 bool rows_fits(const ProjArgs& w, int K, int N, int block_size);
 hipError_t launch_rows_decode(const ProjLaunch& p, bool fc1, int max_rows, int dtype, hipStream_t s);
 
-// Streamed decode projections (R = T*top_k <= 16, E <= 64): every expert's
+// Streamed decode projections (T <= 16, R = T*top_k <= 64, E <= 64): every expert's
 // weights requested at launch and consumed piece by piece as they land; fc1
 // routes the tokens itself and writes the plan.  stream_fits: the projection's
 // shapes, widths and scales suit the kernel.

@@ -299,6 +299,16 @@ STREAM = [
          zp_mode="sym", zpo=math.nan),
     dict(T=4, H=256, I=256, E=4, k=2, fc1_bits=2, fc2_bits=2, block_size=32, dtype=2, act=1,
          zp_mode="zpo", zpo=1.5),
+    # more than 16 routes (at most 16 tokens, 64 routes): every lane of the
+    # first wavefront holds a route while ranking
+    dict(T=16, H=512, I=256, E=32, k=4, fc1_bits=4, fc2_bits=2, block_size=32, dtype=1, act=0,
+         zp_mode="sym", zpo=math.nan),
+    dict(T=12, H=1024, I=512, E=8, k=3, fc1_bits=2, fc2_bits=2, block_size=128, dtype=2, act=1,
+         zp_mode="zpo", zpo=1.5),
+    dict(T=16, H=256, I=512, E=8, k=2, fc1_bits=4, fc2_bits=4, block_size=32, dtype=1, act=0,
+         zp_mode="sym", zpo=math.nan),
+    dict(T=9, H=2048, I=1024, E=16, k=7, fc1_bits=4, fc2_bits=2, block_size=128, dtype=1, act=1,
+         zp_mode="sym", zpo=math.nan),
 ]
 
 
