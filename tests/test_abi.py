@@ -180,3 +180,19 @@ def test_dequantize_validation():
 def test_timer_validation():
     lib = qm.load_library()
     assert lib.qmoe_timer_start(7) == qm.ERR_INVALID_ARG
+
+
+def test_workspace_holds_fc2_k_parts():
+    # prefill layers whose fc2 work-list fills the last round of a 256-unit
+    # grid poorly get room for fc2 K parts: y2 float32 [S, R, H] with S up to 4
+    R, H, I = 4096 * 2, 4096, 14336
+    big = qm.workspace_size(4096, H, I, 8, 2, 2)
+    assert big >= 2 * R * H * 4 + R * I * 2
+    # K = I = 384 holds no two equal parts of whole 128-input super-steps:
+    # one y2 slice
+    R2, H2, I2 = 65536 * 2, 512, 384
+    one = qm.workspace_size(65536, H2, I2, 8, 2, 1)
+    assert R2 * H2 * 4 + R2 * I2 * 2 <= one < 2 * R2 * H2 * 4 + R2 * I2 * 2
+    # decode layers never split
+    dec = qm.workspace_size(8, 2048, 2048, 8, 2, 1)
+    assert dec < 2 * 16 * 2048 * 4 + 16 * 2048 * 2 + 65536
