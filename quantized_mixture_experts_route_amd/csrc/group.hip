@@ -25,35 +25,33 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxExperts = 1024;
 
-// Exclusive scan of v[0..n) in LDS (n <= kMaxExperts) by all threads;
-// returns the total.  `part` is kThreads ints of scratch.
+// Exclusive scan of v[0..n) in LDS (n <= kMaxExperts); returns the total.
+// Wavefront 0 scans 64 values at a time with shuffles and carries the sum
+// from chunk to chunk; the others wait at the one barrier at the end (n is
+// the expert count, so a workgroup-wide scan would cost more barriers than
+// it saves).
 __device__ int block_exclusive_scan(int* v, int n, int* part)
 {
     const int tid = threadIdx.x;
-    const int per = (n + kThreads - 1) / kThreads;  // <= 2
-    const int lo = tid * per;
-    int sum = 0;
-    for (int i = 0; i < per; ++i) {
-        if (lo + i < n) sum += v[lo + i];
-    }
-    part[tid] = sum;
-    __syncthreads();
-    for (int d = 1; d < kThreads; d <<= 1) {  // Hillis-Steele over thread sums
-        const int add = tid >= d ? part[tid - d] : 0;
-        __syncthreads();
-        part[tid] += add;
-        __syncthreads();
-    }
-    const int total = part[kThreads - 1];
-    int run = part[tid] - sum;
-    for (int i = 0; i < per; ++i) {
-        if (lo + i < n) {
-            const int x = v[lo + i];
-            v[lo + i] = run;
-            run += x;
+    if (tid < kWave) {
+        int carry = 0;
+        for (int base = 0; base < n; base += kWave) {
+            const int i = base + tid;
+            const int x = i < n ? v[i] : 0;
+            int incl = x;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const int y = __shfl_up(incl, d, kWave);
+                if (tid >= d) incl += y;
+            }
+            if (i < n) v[i] = carry + incl - x;
+            carry += __shfl(incl, kWave - 1, kWave);
         }
+        if (tid == 0) part[0] = carry;
     }
     __syncthreads();
+    const int total = part[0];
+    __syncthreads();  // part is reused by the next scan
     return total;
 }
 
