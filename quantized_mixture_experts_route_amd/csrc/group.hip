@@ -21,7 +21,7 @@
 namespace qmoe {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxExperts = 1024;
 
