@@ -58,27 +58,41 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(
     }
     __syncthreads();
 
-    // 2) stable rank of every route by expert
-    if (tid < R) {
-        const int e = s_e[tid];
+    // 2) stable rank of every route by expert: four threads per route, each
+    //    counting over a quarter of the table (16-byte reads, all issued at
+    //    once), their counts summed across the four lanes
+    {
+        static_assert(kThreads == 4 * kDecodeMaxRoutes, "four threads per route");
+        const int r = tid >> 2;
+        const int quarter = tid & 3;
+        const int e = s_e[r];
         int less = 0, before = 0, same = 0;
-        const int4* tab = reinterpret_cast<const int4*>(s_e);
+        const int4* tab = reinterpret_cast<const int4*>(s_e) + quarter * (kDecodeMaxRoutes / 16);
 #pragma unroll
-        for (int q4 = 0; q4 < kDecodeMaxRoutes / 4; ++q4) {  // 16-byte reads, all issued at once
+        for (int q4 = 0; q4 < kDecodeMaxRoutes / 16; ++q4) {
             const int4 f = tab[q4];
             const int fs[4] = {f.x, f.y, f.z, f.w};
+            const int r0 = quarter * (kDecodeMaxRoutes / 4) + 4 * q4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 less += fs[i] < e;
                 same += fs[i] == e;
-                before += (fs[i] == e) & (4 * q4 + i < tid);
+                before += (fs[i] == e) & (r0 + i < r);
             }
         }
-        const int pos = less + before;
-        s_route[pos] = tid;
-        s_end[pos] = less + same;
-        // a tile starts every 16 rows of the expert's group
-        s_tile_pos[pos] = (before % kDecodeMT) == 0 ? 1 : 0;
+#pragma unroll
+        for (int d = 1; d < 4; d <<= 1) {
+            less += __shfl_xor(less, d, kWave);
+            same += __shfl_xor(same, d, kWave);
+            before += __shfl_xor(before, d, kWave);
+        }
+        if (quarter == 0 && r < R) {
+            const int pos = less + before;
+            s_route[pos] = r;
+            s_end[pos] = less + same;
+            // a tile starts every 16 rows of the expert's group
+            s_tile_pos[pos] = (before % kDecodeMT) == 0 ? 1 : 0;
+        }
     }
     __syncthreads();
 
