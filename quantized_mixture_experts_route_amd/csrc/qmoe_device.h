@@ -519,6 +519,40 @@ __device__ inline uint64_t wave_max_u64(uint64_t v)
                    max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 
+// Wave maximum of 32-bit unsigned values (same DPP steps as wave_max_u64).
+__device__ inline uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u32<kDppXor1>(v));
+    v = max(v, dpp_u32<kDppXor2>(v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v));
+    v = max(v, dpp_u32<kDppMirror>(v));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
+}
+
+// The same result as wave_max_u64 for words whose low halves differ between
+// lanes (a key in the high half, a distinct index in the low half): the
+// 32-bit maximum of the high halves, then the low half of the one lane that
+// holds it; only when several lanes tie on the high half, a second 32-bit
+// maximum over their low halves.  Two 32-bit reductions at most instead of
+// one on 64-bit pairs.
+__device__ inline uint64_t wave_max_keyed(uint64_t v)
+{
+    const uint32_t hi = (uint32_t)(v >> 32);
+    const uint32_t top = wave_max_u32(hi);
+    const uint64_t holders = __ballot(hi == top);
+    uint32_t lo;
+    if (__popcll(holders) == 1) {
+        lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, (int)__builtin_ctzll(holders));
+    } else {
+        lo = wave_max_u32(hi == top ? (uint32_t)v : 0u);
+    }
+    return ((uint64_t)top << 32) | lo;
+}
+
 __device__ inline float f32_max(float v, float o) { return o > v ? o : v; }
 
 template <int CTRL>

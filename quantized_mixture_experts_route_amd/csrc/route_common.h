@@ -70,7 +70,7 @@ __device__ inline void route_values(int E, int top_k, int normalize, Get get, Em
         for (int j = 0; j < EPL; ++j) {
             best = max_u64(best, cand[j]);
         }
-        best = wave_max_u64(best);
+        best = wave_max_keyed(best);  // words are distinct: each holds its expert index
         const int e = (int)~(uint32_t)best;
         const float v = key_to_logit((int32_t)((uint32_t)(best >> 32) ^ 0x80000000u));
         const float num = expf(v - m);
