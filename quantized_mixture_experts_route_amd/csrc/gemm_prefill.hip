@@ -253,7 +253,11 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
                 load_b(s + 1, sp, bp);
             }
             __syncthreads();
+            // the MFMA phase at raised issue priority, so a wavefront that
+            // reaches it is not held behind its SIMD partner's staging work
+            __builtin_amdgcn_s_setprio(1);
             compute(buf, cur, cbp, s);
+            __builtin_amdgcn_s_setprio(0);
         }
 
         if (!active) continue;
