@@ -82,6 +82,7 @@ void launch_dt(dim3 grid, dim3 block, hipStream_t s, const float* y2, int parts,
     if (top_k <= 2) launch(combine_kernel<DT, 2>, grid, block, s, y2, parts, part_stride, weights, T, H, top_k, o);
     else if (top_k <= 4) launch(combine_kernel<DT, 4>, grid, block, s, y2, parts, part_stride, weights, T, H, top_k, o);
     else if (top_k <= 8) launch(combine_kernel<DT, 8>, grid, block, s, y2, parts, part_stride, weights, T, H, top_k, o);
+    else if (top_k <= 16) launch(combine_kernel<DT, 16>, grid, block, s, y2, parts, part_stride, weights, T, H, top_k, o);
     else launch(combine_kernel<DT, 0>, grid, block, s, y2, parts, part_stride, weights, T, H, top_k, o);
 }
 

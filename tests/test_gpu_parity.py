@@ -382,6 +382,17 @@ def test_layer_single_expert_and_k_equals_e(T):
                               name="k_eq_E"), 4)
 
 
+@pytest.mark.parametrize("k", [3, 6, 12, 20])
+@pytest.mark.parametrize("T", [3, 50])
+def test_layer_combine_slot_bounds(T, k):
+    # top-k of 3, 6 and 12 take the combine that requests 4, 8 and 16 slots at
+    # once, 20 its slot-by-slot loop; T = 3 decodes, T = 50 runs the prefill
+    # tiles
+    spec = synth.custom(T=T, H=256, I=256, E=24, k=k, fc1_bits=4, fc2_bits=2, block_size=32,
+                        dtype=1 + k % 2, name=f"combine_T{T}_k{k}")
+    _layer_check(spec, 1700 + T + k)
+
+
 def test_layer_zero_tokens():
     spec = synth.custom(T=1, H=128, I=128, E=4, k=2)
     dev = dv.to_device(synth.make_inputs(spec, 1), spec)
