@@ -212,8 +212,28 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
         auto compute = [&](const uint32_t* buf, const Span<BITS> (&cur)[4], const RawParams (&cbp)[4],
                            int s) {
             const int kk = s * kSuperK + 32 * g;
+            // the 64-row tile (one wavefront per SIMD when the grid is small)
+            // reads step t + 1's A fragments while step t computes
+            constexpr bool kAhead = MT == 64;
+            auto frag = [&](int mb, int t) {
+                return *reinterpret_cast<const u32x4*>(buf + (mb * 16 + c) * kPitch + 16 * g + 4 * t);
+            };
+            u32x4 next[kAhead ? MB : 1];
+            if constexpr (kAhead) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) next[mb] = frag(mb, 0);
+            }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
+                u32x4 held[kAhead ? MB : 1];
+                if constexpr (kAhead) {
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) held[mb] = next[mb];
+                    if (t + 1 < 4) {
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) next[mb] = frag(mb, t + 1);
+                    }
+                }
                 u32x4 bf[4];
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) {
@@ -223,8 +243,9 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
                 }
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
-                    const u32x4 af = *reinterpret_cast<const u32x4*>(
-                        buf + (mb * 16 + c) * kPitch + 16 * g + 4 * t);
+                    u32x4 af;
+                    if constexpr (kAhead) af = held[mb];
+                    else af = frag(mb, t);
 #pragma unroll
                     for (int nb = 0; nb < 4; ++nb) {
                         acc[mb][nb] = Dt<DT>::mfma(af, bf[nb], acc[mb][nb]);
