@@ -3,24 +3,29 @@
 
 One step = one qmoe_forward call (route, group, fc1 + activation, fc2,
 combine) over one batch of synthetic inputs already resident in HBM.  The
-default workload is the int2 GeGLU decode layer (T=8, hidden=inter=2048,
-E=8, top-2, block 128, fractional zero point 1.5, fp16); ``--workload N``
-selects another of the five named workloads.
+headline line runs the large skewed prefill layer (T=4096, hidden=4096,
+inter=14336, E=8, top-2, int4, block 128, bf16), the largest of the five
+workloads; ``per_config`` holds the same measurement for every workload
+(tiny int4, int2 GeGLU decode, int4 + u8 zero-point prefill, 512-expert
+int3/int2 decode, skewed prefill).
 
-To keep the weights from being served by the 256 MB Infinity Cache, each step
-uses the next of C identical copies of the expert weights (C copies span
->= 1 GiB), so every step streams its weights from HBM.
+Timing protocol, per workload:
+- before every call (warm-up and timed), a 1 GiB buffer is read, so the L2
+  and the 256 MB Infinity Cache hold none of the layer's weights or inputs;
+- a HIP event pair on the call's stream brackets each timed call (the flush
+  is outside it); per-call times give mean, median, p10 and p90; the host
+  wall clock over the timed loop is reported beside them;
+- the fc1 and fc2 kernels' average durations come from event pairs that the
+  library records in those kernels' own dispatch packets, over as many
+  further calls under the same protocol.
 
-Prints one JSON line: tokens/s over the timed steps, the dominant kernel's
-roofline (fc1: packed-weight bytes of the selected experts per launch for
-decode -> GB/s vs 8 TB/s; 2*R*H*2I flops per launch for prefill -> TFLOP/s vs
-2.5 PFLOP/s dense fp16/bf16), and the CPU oracle timed on the host cores on a
-bounded sample as a baseline.
-
-The timed region runs the steps with nothing else on the stream; the fc1
-kernel's average duration comes from a second pass over the same number of
-steps with a HIP event pair around each fc1 launch (on the library's stream),
-so the event overhead does not enter the step time.
+Rooflines: ``roofline`` is the dominant kernel, fc1 (decode: packed-weight
+bytes of the selected experts per launch over 8 TB/s; prefill: 4*R*H*I flops
+per launch over 2.5 PFLOP/s dense bf16/fp16).  ``gemm_roofline`` is the
+layer's two grouped projections together (decode: fc1 + fc2 packed bytes
+over the summed durations; prefill: 6*R*H*I flops over the summed
+durations).  ``cpu_baseline`` is the double-precision CPU oracle timed on the
+host cores on a bounded token sample of the headline workload.
 
 --calibrate-copy adds one elementwise kernel of known traffic (neg of a 256
 MiB float32 tensor: 256 MiB read, 256 MiB written) before the timed region,
@@ -31,7 +36,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -49,14 +53,22 @@ METRIC = "QMoE layer tokens/s; decode HBM GB/s and prefill TFLOP/s vs MI355X pea
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+HEADLINE = 5
+FLUSH_BYTES = 1 << 30
+CALIBRATION_BYTES = 256 << 20
 
 
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=HEADLINE, choices=[1, 2, 3, 4, 5],
+                    help="workload of the headline line")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="measure the headline workload only")
+    ap.add_argument("--min-steps-per-config", type=int, default=100,
+                    help="per_config entries time at least this many calls")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -67,9 +79,9 @@ def _args():
     ap.add_argument("--pmc-summary", metavar="DIR",
                     help="summarize rocprofv3 CSV files under DIR and exit")
     ap.add_argument("--graph", action="store_true",
-                    help="also time the layer replayed from HIP graphs (one per weight copy)")
+                    help="also time the headline layer replayed from a HIP graph")
     ap.add_argument("--stages", action="store_true",
-                    help="also time every stage separately after the timed region")
+                    help="also time every stage of the headline layer separately")
     return ap.parse_args()
 
 
@@ -96,17 +108,13 @@ def _proj_bytes(p: qm.Projection) -> int:
     return n
 
 
-def _copy_proj(p: qm.Projection) -> qm.Projection:
-    return qm.Projection(p.codes.clone(), p.scales.clone(),
-                         None if p.zero_points is None else p.zero_points.clone(), p.bits)
-
-
 def _cpu_baseline(inp, spec, min_seconds):
     """The oracle on a bounded token sample, repeated to >= min_seconds."""
     import oracle
     T = spec["T"]
-    per_token = 6.0 * spec["k"] * spec["H"] * spec["I"]
-    n_tok = int(max(1, min(T, 2.5e9 // per_token)))  # keep one pass to a few seconds
+    host_cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", host_cores))
+    n_tok = min(T, threads)  # one token per thread and pass, every thread busy
     tokens = np.linspace(0, T - 1, n_tok).astype(np.int64)
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -115,13 +123,10 @@ def _cpu_baseline(inp, spec, min_seconds):
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     return {"value": round(reps * n_tok / el, 4), "unit": "tokens/s",
-            "cores": min(threads, n_tok), "kind": "oracle",
-            "sample": f"{n_tok} of {T} tokens, {reps} passes, {el:.1f} s, double precision"}
-
-
-CALIBRATION_BYTES = 256 << 20
+            "cores": min(threads, n_tok), "host_cores": host_cores, "kind": "oracle",
+            "sample": f"{n_tok} of {T} tokens of {spec['name']}, {reps} passes, {el:.1f} s, "
+                      f"double precision, OpenMP over tokens"}
 
 
 def kernel_source_digest():
@@ -143,6 +148,7 @@ def _pmc_summary(root):
     import csv
     import glob
     from collections import defaultdict
+
     def short(name):
         return name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
 
@@ -169,6 +175,128 @@ def _pmc_summary(root):
                   f"| {float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
 
 
+class Layer:
+    """One workload's inputs on the device and a callable layer step."""
+
+    def __init__(self, cfg, dev):
+        self.cfg = cfg
+        self.spec = spec = synth.workload(cfg)
+        self.inp = synth.make_inputs(spec, synth.seed_for(cfg))
+        self.hidden, self.logits, self.projs = _to_device(self.inp, spec, dev)
+        T, H, I, E, k = spec["T"], spec["H"], spec["I"], spec["E"], spec["k"]
+        self.ws = qm.alloc_workspace(T, H, I, E, k, qm.dtype_code(self.hidden.dtype), dev)
+        self.out = torch.empty_like(self.hidden)
+        self.decode = T * k <= qm.DECODE_MAX_ROUTES
+
+    def __call__(self):
+        s = self.spec
+        qm.forward(self.hidden, self.logits, self.projs["fc1"], self.projs["fc2"], top_k=s["k"],
+                   block_size=s["block_size"], normalize=s["normalize"], activation=s["act"],
+                   zero_point_offset=s["zpo"], out=self.out, workspace=self.ws)
+
+
+class Flush:
+    """Reads a 1 GiB buffer: afterwards no cache level holds the layer's data."""
+
+    def __init__(self, dev):
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        self.acc = torch.empty((), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        torch.sum(self.buf, dim=0, out=self.acc)
+
+
+def _time_calls(step, flush, steps, warmup):
+    """Per-call HIP event times (ms) of `steps` calls, each after a cache flush."""
+    for _ in range(warmup):
+        flush()
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush()
+        starts[i].record()
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]), wall
+
+
+def _stage_avg(step, flush, stage, steps):
+    """Average duration (ms) of one stage's kernel, from event pairs in its dispatch packets."""
+    qm.timer_start(stage)
+    for _ in range(steps):
+        flush()
+        step()
+    ms, n = qm.timer_stop()
+    return ms / max(n, 1), n
+
+
+def _traffic(name):
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    with open(PROFILE_TRAFFIC) as f:
+        rec = json.load(f).get(name)
+    if isinstance(rec, dict) and rec.get("kernel_source_sha256") == kernel_source_digest():
+        return rec.get("bytes_per_launch")
+    return None
+
+
+def measure(layer: Layer, flush, steps, warmup):
+    spec = layer.spec
+    T, H, I, E, k = spec["T"], spec["H"], spec["I"], spec["E"], spec["k"]
+    per_call, wall = _time_calls(layer, flush, steps, warmup)
+    fc1_ms, _ = _stage_avg(layer, flush, qm.STAGE_FC1, steps)
+    fc2_ms, _ = _stage_avg(layer, flush, qm.STAGE_FC2, steps)
+    ids, _ = qm.route(layer.logits, k, spec["normalize"])
+    selected = int(torch.unique(ids).numel())
+    mean_ms = float(per_call.mean())
+    entry = {
+        "workload": spec["name"], "T": T, "H": H, "I": I, "E": E, "top_k": k,
+        "fc1_bits": spec["fc1_bits"], "fc2_bits": spec["fc2_bits"],
+        "block_size": spec["block_size"], "dtype": "f16" if spec["dtype"] == 1 else "bf16",
+        "path": "decode" if layer.decode else "prefill", "selected_experts": selected,
+        "steps": steps, "warmup": warmup,
+        "tokens_per_s": round(T / (mean_ms * 1e-3), 2),
+        "layer_ms": {"mean": round(mean_ms, 5), "median": round(float(np.median(per_call)), 5),
+                     "p10": round(float(np.percentile(per_call, 10)), 5),
+                     "p90": round(float(np.percentile(per_call, 90)), 5),
+                     "wall_mean": round(wall * 1e3 / steps, 5)},
+        "fc1_ms": round(fc1_ms, 5), "fc2_ms": round(fc2_ms, 5),
+    }
+    if layer.decode:
+        b1 = selected * (_proj_bytes(layer.projs["fc1"]) // E)
+        b2 = selected * (_proj_bytes(layer.projs["fc2"]) // E)
+        a1 = b1 / (fc1_ms * 1e-3) / 1e9
+        ag = (b1 + b2) / ((fc1_ms + fc2_ms) * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(a1, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a1 / HBM_PEAK_GBS, 4), "kernel": "fc1 (+ gated activation)",
+                "kernel_avg_ms": round(fc1_ms, 5), "work_per_launch": b1,
+                "work_unit": "packed weight bytes (codes + scales + zero points) of the selected experts"}
+        gemm = {"bound": "hbm", "achieved": round(ag, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ag / HBM_PEAK_GBS, 4), "kernels": "fc1 + fc2",
+                "ms": round(fc1_ms + fc2_ms, 5), "work": b1 + b2}
+    else:
+        f1 = 4.0 * T * k * H * I
+        fl = 6.0 * T * k * H * I
+        a1 = f1 / (fc1_ms * 1e-3) / 1e12
+        ag = fl / ((fc1_ms + fc2_ms) * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(a1, 1), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(a1 / MFMA_PEAK_TFLOPS, 4),
+                "kernel": "fc1 (+ gated activation)", "kernel_avg_ms": round(fc1_ms, 5),
+                "work_per_launch": f1, "work_unit": "flops 2*R*H*2I"}
+        gemm = {"bound": "mfma", "achieved": round(ag, 1), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ag / MFMA_PEAK_TFLOPS, 4),
+                "kernels": "fc1 + fc2", "ms": round(fc1_ms + fc2_ms, 5), "work": fl}
+    roof["traffic"] = _traffic(spec["name"])
+    entry["roofline"] = roof
+    entry["gemm_roofline"] = gemm
+    return entry
+
+
 def main():
     a = _args()
     if a.digest:
@@ -182,28 +310,10 @@ def main():
               "(the layer's multi-GPU expert-parallel sharding is a design, not built)",
               file=sys.stderr)
         sys.exit(2)
-    spec = synth.workload(a.workload)
-    decode = spec["T"] * spec["k"] <= qm.DECODE_MAX_ROUTES
-    steps = a.steps if a.steps is not None else (200 if decode else (20 if spec["T"] > 1024 else 100))
-    warmup = a.warmup if a.warmup is not None else max(3, steps // 10)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    inp = synth.make_inputs(spec, synth.seed_for(a.workload))
-    hidden, logits, projs = _to_device(inp, spec, dev)
-    T, H, I, E, k = spec["T"], spec["H"], spec["I"], spec["E"], spec["k"]
-    per_copy = _proj_bytes(projs["fc1"]) + _proj_bytes(projs["fc2"])
-    copies = int(min(64, max(2, math.ceil((1 << 30) / per_copy))))
-    fc1s = [projs["fc1"]] + [_copy_proj(projs["fc1"]) for _ in range(copies - 1)]
-    fc2s = [projs["fc2"]] + [_copy_proj(projs["fc2"]) for _ in range(copies - 1)]
-    dt = qm.dtype_code(hidden.dtype)
-    ws = qm.alloc_workspace(T, H, I, E, k, dt, dev)
-    out = torch.empty_like(hidden)
-
-    def step(i):
-        qm.forward(hidden, logits, fc1s[i % copies], fc2s[i % copies], top_k=k,
-                   block_size=spec["block_size"], normalize=spec["normalize"],
-                   activation=spec["act"], zero_point_offset=spec["zpo"], out=out, workspace=ws)
+    qm.load_library()
+    flush = Flush(dev)
 
     if a.calibrate_copy:
         src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
@@ -212,104 +322,70 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(warmup + i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / steps
-
-    # fc1 kernel duration: HIP events around each fc1 launch over another
-    # `steps` steps (same weight rotation)
-    qm.timer_start(qm.STAGE_FC1)
-    for i in range(steps):
-        step(warmup + steps + i)
-    fc1_ms, fc1_n = qm.timer_stop()
-    fc1_avg_ms = fc1_ms / max(fc1_n, 1)
-
-    # algorithmic work of one fc1 launch
-    ids, _ = qm.route(logits, k, spec["normalize"])
-    selected = torch.unique(ids).numel()
-    fc1 = projs["fc1"]
-    if decode:
-        per_expert = _proj_bytes(fc1) // E
-        work = selected * per_expert
-        achieved = work / (fc1_avg_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        work = 2.0 * T * k * H * (2 * I)
-        achieved = work / (fc1_avg_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4)}
-    roof["kernel"] = "fc1 (+ gated activation)"
-    roof["kernel_avg_ms"] = round(fc1_avg_ms, 5)
-    traffic = None
-    if os.path.exists(PROFILE_TRAFFIC):
-        with open(PROFILE_TRAFFIC) as f:
-            traffic = json.load(f).get(spec["name"])
-    if isinstance(traffic, dict) and traffic.get("kernel_source_sha256") == kernel_source_digest():
-        roof["traffic"] = traffic.get("bytes_per_launch")
-    else:
-        roof["traffic"] = None
-
+    head = Layer(a.workload, dev)
+    print(f"# {head.spec['name']}: {a.warmup} warm-up + {a.steps} timed calls", file=sys.stderr,
+          flush=True)
+    h = measure(head, flush, a.steps, a.warmup)
+    props = torch.cuda.get_device_properties(dev)
     result = {
-        "metric": METRIC, "value": round(T / (ms_per_step * 1e-3), 2), "unit": "tokens/s",
-        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16" if spec["dtype"] == 1 else "bf16", "data": "synthetic",
-        "config": {"workload": spec["name"], "T": T, "H": H, "I": I, "E": E, "top_k": k,
-                   "fc1_bits": spec["fc1_bits"], "fc2_bits": spec["fc2_bits"],
-                   "block_size": spec["block_size"], "path": "decode" if decode else "prefill",
-                   "selected_experts": selected, "weight_copies": copies,
-                   "parallelism": "single GPU"},
-        "roofline": roof,
+        "metric": METRIC, "value": h["tokens_per_s"], "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": h["layer_ms"]["mean"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": h["dtype"], "data": "synthetic",
+        "config": {"workload": h["workload"], "T": h["T"], "H": h["H"], "I": h["I"],
+                   "E": h["E"], "top_k": h["top_k"], "fc1_bits": h["fc1_bits"],
+                   "fc2_bits": h["fc2_bits"], "block_size": h["block_size"], "path": h["path"],
+                   "selected_experts": h["selected_experts"], "parallelism": "single GPU"},
+        "timing": dict(h["layer_ms"], method="HIP event pair per call on the call's stream, "
+                       "1 GiB read before every call (outside the pair)"),
+        "roofline": h["roofline"],
+        "gemm_roofline": h["gemm_roofline"],
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "compute_units": props.multi_processor_count},
     }
 
     if a.graph:
-        # one captured layer per weight copy, replayed in the same rotation
-        graphs = []
+        graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step(0)
+            head()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        for c in range(copies):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(c)
-            graphs.append(g)
-        for i in range(warmup):
-            graphs[i % copies].replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            graphs[(warmup + i) % copies].replay()
-        torch.cuda.synchronize()
-        g_ms = (time.perf_counter() - t0) * 1e3 / steps
-        result["graph_replay"] = {"ms_per_step": round(g_ms, 5),
-                                  "tokens_per_s": round(T / (g_ms * 1e-3), 2)}
-        del graphs
+        with torch.cuda.graph(graph):
+            head()
+        per_call, _ = _time_calls(graph.replay, flush, a.steps, a.warmup)
+        result["graph_replay_ms"] = {"mean": round(float(per_call.mean()), 5),
+                                     "median": round(float(np.median(per_call)), 5)}
+        del graph
 
     if a.stages:
         stage_ms = {}
         for name, st in (("route", qm.STAGE_ROUTE), ("group", qm.STAGE_GROUP),
                          ("fc1", qm.STAGE_FC1), ("fc2", qm.STAGE_FC2),
                          ("combine", qm.STAGE_COMBINE)):
-            qm.timer_start(st)
-            for i in range(steps):
-                step(i)
-            ms, n = qm.timer_stop()
-            stage_ms[name] = round(ms / max(n, 1), 5)
+            ms, _ = _stage_avg(head, flush, st, a.steps)
+            stage_ms[name] = round(ms, 5)
         result["stage_avg_ms"] = stage_ms
 
+    if not a.no_per_config:
+        per = {}
+        for cfg in (1, 2, 3, 4, 5):
+            if cfg == a.workload:
+                per[h["workload"]] = h
+                continue
+            layer = Layer(cfg, dev)
+            steps = max(a.steps, a.min_steps_per_config)
+            print(f"# {layer.spec['name']}: {steps} timed calls", file=sys.stderr, flush=True)
+            e = measure(layer, flush, steps, max(a.warmup, 10))
+            per[e["workload"]] = e
+            del layer
+            torch.cuda.empty_cache()
+        result["per_config"] = per
+
     if not a.no_cpu_baseline:
-        result["cpu_baseline"] = _cpu_baseline(inp, spec, a.cpu_seconds)
+        print("# CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = _cpu_baseline(head.inp, head.spec, a.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

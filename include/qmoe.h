@@ -112,7 +112,11 @@ int qmoe_route(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t
                int32_t* topk_ids, float* topk_weights, void* stream);
 
 /* Work-list capacity (items) that always suffices for qmoe_group with these
- * arguments: (ceil(R/m_tile) + min(E, R)) * ceil(N/n_tile), R = T*top_k. */
+ * arguments: (ceil(R/m_tile) + min(E, R)) * ceil(N/n_tile), R = T*top_k
+ * [gemm_quant_moe.rs, moe_build_tile_worklist: one item per m-tile and
+ * n-tile of every expert that has rows; with at most min(E, R) such experts,
+ * each contributes at most one partial m-tile beyond ceil(R/m_tile)].
+ * Returns -1 on invalid arguments or overflow. */
 int64_t qmoe_worklist_capacity(int64_t T, int32_t top_k, int32_t E, int32_t m_tile,
                                int32_t n_tile, int32_t N);
 
@@ -139,7 +143,12 @@ int qmoe_group(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int
                int32_t n_tile, int32_t N, int32_t* expert_offsets, int32_t* sorted_routes,
                int32_t* worklist, int64_t worklist_capacity, int32_t* n_items, void* stream);
 
-/* Workspace bytes qmoe_forward needs for these sizes (0 on invalid sizes). */
+/* Workspace bytes qmoe_forward needs for these sizes (0 on invalid sizes)
+ * [qmoe.rs, QMoEKernel::execute sizes its scratch pool (route ids and
+ * weights, fc1 and activation rows, route outputs, grouping arrays) from the
+ * shapes alone; moe.rs, the MoE workspace estimator].  The layout depends on
+ * neither the weight widths nor block_size, so unlike those estimators this
+ * takes no bits or block_size argument. */
 size_t qmoe_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t top_k,
                            int32_t dtype);
 
@@ -165,12 +174,19 @@ size_t qmoe_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t t
  * bits in {2,3,4} per projection, T*H < 2^32 and T*top_k*I < 2^32 (the
  * projection kernels address their inputs with 32-bit element offsets).
  * T = 0 returns QMOE_OK and enqueues nothing.
- * Numerics: dequantized weights are rounded to dtype (round to nearest even)
- * before the products, products accumulate in float32, the activation is
- * rounded to dtype, fc2 outputs stay float32 until the combine.  For many
- * routes, fc2 may split its K range into 2 or 4 parts (chosen from the sizes
- * alone); their float32 partial sums are added in part order before the
- * routing weights apply, so results stay deterministic.
+ * Numerics: products accumulate in float32, the activation is rounded to
+ * dtype, fc2 outputs stay float32 until the combine.  The prefill kernels
+ * (T*top_k > QMOE_DECODE_MAX_ROUTES) and the decode kernels for block sizes
+ * below 128 round each dequantized weight (code - zp) * scale once to dtype
+ * (round to nearest even) before the products [PR 33569: dequantized weights
+ * rounded to the activation type before accumulation].  The decode kernels
+ * for block sizes that are multiples of 128 feed the MFMA the exact codes
+ * (biased into dtype values, see qmoe_raw_codes) and apply zero point and
+ * scale to the float32 partial sums of each 128-input step, so W is never
+ * rounded there.  For many routes, fc2 may split its K range into 2 or 4
+ * parts (chosen from the sizes alone); their float32 partial sums are added
+ * in part order before the routing weights apply, so results stay
+ * deterministic.
  */
 int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, int32_t I,
                  int32_t E, const qmoe_proj* fc1, const qmoe_proj* fc2, float zero_point_offset,
@@ -179,16 +195,44 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Test hook: the dequantization the projections use, written out in full.
- *   p           one projection as above (E experts, N rows, K inputs)
+ * Test hook: the dequantization of the weight-rounding kernels, written out
+ * in full [qmoe.rs, decode_affine_weight: (code - zp) * scale with the code
+ * read LSB-first and the zero point from the tensor or the centre; PR 32198,
+ * zero_point_offset as the zero point of every block].
+ *   p           one projection as above (E experts, N rows, K inputs, K a
+ *               multiple of 32 and of block_size)
  *   codes_out   NULL or int32 [E, N, K] out: unpacked codes
  *   w_out       dtype [E, N, K] out: round-to-nearest-even of (code - zp) * scale
- * The kernels that run the projections call the same device unpack and
- * dequant routines.
+ * The prefill kernels and the decode kernels for block sizes below 128 call
+ * the same device unpack and dequant routines (the raw-code decode path is
+ * covered by qmoe_raw_codes).  Errors: QMOE_ERR_INVALID_ARG for bad sizes,
+ * pointers or dtype; QMOE_ERR_UNSUPPORTED for K not a multiple of 32.
  */
 int qmoe_dequantize(const qmoe_proj* p, int32_t E, int32_t N, int32_t K, int32_t block_size,
                     float zero_point_offset, int32_t dtype, int32_t* codes_out, void* w_out,
                     void* stream);
+
+/*
+ * Test hook: the codes as the decode kernels' raw-code MFMA operands carry
+ * them [qmoe.rs, decode_affine_weight, LSB-first code order; PR 33569, 24-bit
+ * 8-code INT3 groups].  For block sizes that are multiples of 128 the decode
+ * kernels place each code in the mantissa of a dtype value base + code
+ * (exact) and take base and zero point out of the float32 sums.  This runs the
+ * same device routines on every 32-code span and writes base + code - base,
+ * i.e. the code each MFMA input carries, at its input position.
+ *   p           one projection (only codes and bits are read)
+ *   variant     QMOE_RAW_SINGLE_BASE: one base per dtype (fp16 1024, bf16
+ *               128), the m-tile and expert-stationary decode kernels, 2/3/4
+ *               bits; QMOE_RAW_MULTI_BASE: a power-of-two base per register,
+ *               the streamed decode kernels, 2/4 bits
+ *   codes_out   int32 [E, N, K] out
+ * Requires K a multiple of 32.  Errors as qmoe_dequantize; 3-bit codes with
+ * QMOE_RAW_MULTI_BASE return QMOE_ERR_UNSUPPORTED.
+ */
+#define QMOE_RAW_SINGLE_BASE 0
+#define QMOE_RAW_MULTI_BASE 1
+int qmoe_raw_codes(const qmoe_proj* p, int32_t E, int32_t N, int32_t K, int32_t dtype,
+                   int32_t variant, int32_t* codes_out, void* stream);
 
 /*
  * Kernel timer for measurement.  After qmoe_timer_start(stage), every

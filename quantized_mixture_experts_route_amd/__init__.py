@@ -31,10 +31,12 @@ ACT_SWIGLU = 0
 ACT_GEGLU = 1
 DECODE_MAX_ROUTES = 80
 STAGE_ROUTE, STAGE_GROUP, STAGE_FC1, STAGE_FC2, STAGE_COMBINE = range(5)
+RAW_SINGLE_BASE = 0
+RAW_MULTI_BASE = 1
 
 EXPORTED = ("qmoe_last_error", "qmoe_route", "qmoe_worklist_capacity", "qmoe_group",
-            "qmoe_workspace_size", "qmoe_forward", "qmoe_dequantize", "qmoe_timer_start",
-            "qmoe_timer_stop")
+            "qmoe_workspace_size", "qmoe_forward", "qmoe_dequantize", "qmoe_raw_codes",
+            "qmoe_timer_start", "qmoe_timer_stop")
 
 
 class QMoEError(RuntimeError):
@@ -74,9 +76,10 @@ def load_library(path: str = LIB_PATH):
                                  ctypes.POINTER(_Proj), f32, i32, i32, i32, i32, i32, P, P, P, P,
                                  sz, P]
     lib.qmoe_dequantize.argtypes = [ctypes.POINTER(_Proj), i32, i32, i32, i32, f32, i32, P, P, P]
+    lib.qmoe_raw_codes.argtypes = [ctypes.POINTER(_Proj), i32, i32, i32, i32, i32, P, P]
     lib.qmoe_timer_start.argtypes = [i32]
     lib.qmoe_timer_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
-    for name in ("qmoe_route", "qmoe_group", "qmoe_forward", "qmoe_dequantize",
+    for name in ("qmoe_route", "qmoe_group", "qmoe_forward", "qmoe_dequantize", "qmoe_raw_codes",
                  "qmoe_timer_start", "qmoe_timer_stop"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -204,6 +207,10 @@ def forward(hidden: torch.Tensor, logits: torch.Tensor, fc1: Projection, fc2: Pr
     if logits.shape[0] != T:
         raise ValueError("logits rows must equal hidden rows")
     E = logits.shape[1]
+    for name, proj in (("fc1", fc1), ("fc2", fc2)):
+        # the library reads scales as the layer's dtype; another dtype's bits would be misread
+        if proj.scales.dtype != hidden.dtype:
+            raise ValueError(f"{name}.scales has dtype {proj.scales.dtype}, expected {hidden.dtype}")
     I = fc2.codes.shape[2] * 8 // fc2.bits
     p1 = fc1._struct(E, 2 * I, H, block_size, "fc1")
     p2 = fc2._struct(E, H, I, block_size, "fc2")
@@ -227,6 +234,8 @@ def forward(hidden: torch.Tensor, logits: torch.Tensor, fc1: Projection, fc2: Pr
 def dequantize(proj: Projection, E: int, N: int, K: int, block_size: int, dtype: torch.dtype,
                zero_point_offset: float = math.nan, want_codes: bool = True, stream=None):
     """Unpacked codes (int32 [E, N, K] or None) and dequantized weights (dtype [E, N, K])."""
+    if proj.scales.dtype != dtype:
+        raise ValueError(f"scales have dtype {proj.scales.dtype}, expected {dtype}")
     p = proj._struct(E, N, K, block_size, "projection")
     dev = proj.codes.device
     w = torch.empty((E, N, K), dtype=dtype, device=dev)
@@ -235,6 +244,16 @@ def dequantize(proj: Projection, E: int, N: int, K: int, block_size: int, dtype:
                                           float(zero_point_offset), dtype_code(dtype), _ptr(q),
                                           _ptr(w), _stream(stream)))
     return q, w
+
+
+def raw_codes(proj: Projection, E: int, N: int, K: int, block_size: int, dtype: torch.dtype,
+              variant: int = RAW_SINGLE_BASE, stream=None):
+    """int32 [E, N, K]: the codes the decode kernels' raw-code MFMA operands carry."""
+    p = proj._struct(E, N, K, block_size, "projection")
+    q = torch.empty((E, N, K), dtype=torch.int32, device=proj.codes.device)
+    _check(load_library().qmoe_raw_codes(ctypes.byref(p), E, N, K, dtype_code(dtype), variant,
+                                         _ptr(q), _stream(stream)))
+    return q
 
 
 def timer_start(stage: int):

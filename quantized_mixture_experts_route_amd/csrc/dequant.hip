@@ -1,8 +1,11 @@
-// dequant.hip -- the projections' dequantization written out to memory, as a
-// test hook.  One thread per 32-code span calls the same span load, zero-point
-// and dequant_step / dequant_step_generic routines the projection kernels use,
-// then stores every value at its input position (undoing the register order
-// of code_order<DT, BITS>()).
+// dequant.hip -- the projections' unpacking and dequantization written out to
+// memory, as test hooks.  One thread per 32-code span calls the same span
+// load, zero-point and dequant_step / dequant_step_generic routines the
+// prefill and row-block kernels use (dequant_kernel), or the raw-code
+// routines of the decode kernels whose blocks span whole 128-input
+// super-steps (raw_codes_kernel: raw_step with one base, raw_step_based with
+// a base per register), then stores every value at its input position
+// (undoing the register order of code_order / raw_order).
 #include "gemm_common.h"
 
 namespace qmoe {
@@ -40,6 +43,48 @@ __global__ __launch_bounds__(256) void dequant_kernel(ProjArgs w, int64_t rows, 
     }
 }
 
+// The codes as the raw-code MFMA operands carry them: each 16-bit half is the
+// dtype value base + code, exact, so subtracting the base in float32 gives the
+// code back.  MULTI: raw_step_based with the streamed kernels' per-register
+// bases (2- and 4-bit codes); otherwise raw_step with the single bias.
+template <int DT, int BITS, bool MULTI>
+__global__ __launch_bounds__(256) void raw_codes_kernel(const uint8_t* __restrict__ codes,
+                                                        int64_t rows, int K,
+                                                        int32_t* __restrict__ codes_out)
+{
+    constexpr Order O = raw_order<BITS>();
+    const int spans = K / 32;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * spans) return;
+    const int64_t row = idx / spans;
+    const int k0 = (int)(idx % spans) * 32;
+    const Span<BITS> sp = load_span<BITS>(codes + row * (int64_t)(K * BITS / 8), k0);
+    uint32_t magic[4];
+    float base[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if constexpr (MULTI) {
+            magic[r] = opaque(raw_magic<DT, BITS>(r));
+            base[r] = raw_base<DT, BITS>(r);
+        } else {
+            magic[r] = opaque(DT == kF16 ? 0x64006400u : 0x43004300u);
+            base[r] = raw_bias<DT>();
+        }
+    }
+    int32_t* out = codes_out + row * K + k0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        u32x4 v;
+        if constexpr (MULTI) v = raw_step_based<DT, BITS>(sp, t, magic);
+        else v = raw_step<DT, BITS>(sp, t, magic[0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            out[order_lo(O, t, r)] = (int32_t)(Dt<DT>::to_float((uint16_t)(v[r] & 0xffffu)) - base[r]);
+            out[order_hi(O, t, r)] = (int32_t)(Dt<DT>::to_float((uint16_t)(v[r] >> 16)) - base[r]);
+        }
+    }
+}
+
 template <int DT, int BITS>
 hipError_t launch_zp(const ProjArgs& w, int64_t rows, int K, int block_size, int32_t* codes_out,
                      uint16_t* w_out, hipStream_t s)
@@ -66,7 +111,42 @@ hipError_t launch_dt(const ProjArgs& w, int64_t rows, int K, int block_size, int
     }
 }
 
+template <int DT, int BITS>
+hipError_t launch_raw_bits(const uint8_t* codes, int64_t rows, int K, bool multi, int32_t* out,
+                           hipStream_t s)
+{
+    const int64_t n = rows * (K / 32);
+    const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+    if constexpr (BITS == 3) {
+        if (multi) return hipErrorInvalidValue;  // the streamed kernels take 2- and 4-bit codes
+        launch(raw_codes_kernel<DT, BITS, false>, grid, block, s, codes, rows, K, out);
+    } else {
+        if (multi) launch(raw_codes_kernel<DT, BITS, true>, grid, block, s, codes, rows, K, out);
+        else launch(raw_codes_kernel<DT, BITS, false>, grid, block, s, codes, rows, K, out);
+    }
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_raw_dt(const uint8_t* codes, int bits, int64_t rows, int K, bool multi,
+                         int32_t* out, hipStream_t s)
+{
+    switch (bits) {
+    case 2: return launch_raw_bits<DT, 2>(codes, rows, K, multi, out, s);
+    case 3: return launch_raw_bits<DT, 3>(codes, rows, K, multi, out, s);
+    case 4: return launch_raw_bits<DT, 4>(codes, rows, K, multi, out, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_raw_codes(const uint8_t* codes, int bits, int64_t rows, int K, int dtype,
+                            bool multi, int32_t* codes_out, hipStream_t s)
+{
+    return dtype == kBF16 ? launch_raw_dt<kBF16>(codes, bits, rows, K, multi, codes_out, s)
+                          : launch_raw_dt<kF16>(codes, bits, rows, K, multi, codes_out, s);
+}
 
 hipError_t launch_dequant(const ProjArgs& w, int64_t rows, int K, int block_size, int dtype,
                           int32_t* codes_out, void* w_out, hipStream_t s)

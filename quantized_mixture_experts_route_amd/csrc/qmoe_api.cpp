@@ -526,6 +526,29 @@ int qmoe_dequantize(const qmoe_proj* p, int32_t E, int32_t N, int32_t K, int32_t
     return e == hipSuccess ? ok() : hip_fail(e, "dequant launch");
 }
 
+int qmoe_raw_codes(const qmoe_proj* p, int32_t E, int32_t N, int32_t K, int32_t dtype,
+                   int32_t variant, int32_t* codes_out, void* stream)
+{
+    int rc;
+    if ((rc = check_proj("projection", p))) return rc;
+    if (E < 1 || N < 1 || K < 1) return fail(QMOE_ERR_INVALID_ARG, "E, N, K must be >= 1");
+    if (K % 32) return fail(QMOE_ERR_UNSUPPORTED, "K=%d must be a multiple of 32", K);
+    if (dtype != QMOE_DTYPE_F16 && dtype != QMOE_DTYPE_BF16) return fail(QMOE_ERR_INVALID_ARG, "bad dtype");
+    if (variant != QMOE_RAW_SINGLE_BASE && variant != QMOE_RAW_MULTI_BASE) {
+        return fail(QMOE_ERR_INVALID_ARG, "variant=%d is neither SINGLE_BASE (0) nor MULTI_BASE (1)", variant);
+    }
+    if (variant == QMOE_RAW_MULTI_BASE && p->bits == 3) {
+        return fail(QMOE_ERR_UNSUPPORTED, "the multi-base raw codes take 2- and 4-bit codes only");
+    }
+    if (!codes_out || !aligned(codes_out, 4)) return fail(QMOE_ERR_INVALID_ARG, "codes_out must be non-NULL");
+    int64_t rows, elems;
+    if (!mul_ok(E, N, &rows) || !mul_ok(rows, K, &elems)) return fail(QMOE_ERR_INVALID_ARG, "size overflow");
+    const hipError_t e = qmoe::launch_raw_codes(p->codes, p->bits, rows, K, dtype,
+                                                variant == QMOE_RAW_MULTI_BASE, codes_out,
+                                                (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "raw codes launch");
+}
+
 int qmoe_timer_start(int32_t stage)
 {
     if (stage < QMOE_STAGE_ROUTE || stage > QMOE_STAGE_COMBINE) {

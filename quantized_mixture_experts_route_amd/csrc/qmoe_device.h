@@ -439,6 +439,56 @@ __device__ inline u32x4 raw_step(const Span<BITS>& sp, int t, uint32_t magic)
     return out;
 }
 
+// Multi-base raw codes (the streamed decode kernels): register r of an MFMA step takes its code pair from the packed
+// word shifted right by raw_shift(r), at bits raw_pos(r) and raw_pos(r) + 16:
+// int2 pairs sit 2r bits up (8 more on odd steps, taken out first), int4
+// pairs 4(r & 1) bits up (8 more for r >= 2).  Fields must stay inside the
+// mantissa (10 bits fp16, 7 bits bf16), so bf16 moves int2's fourth pair and
+// int4's odd pairs down first.  The base is the power of two whose mantissa
+// gives bit raw_pos(r) weight 1: 2^(m - raw_pos(r)).
+template <int DT, int BITS>
+__host__ __device__ constexpr int raw_shift(int r)
+{
+    if (BITS == 2) return (DT == kF16 || r < 3) ? 0 : 2;
+    return (r < 2 ? 0 : 8) + ((DT == kBF16 && (r & 1)) ? 1 : 0);
+}
+
+template <int DT, int BITS>
+__host__ __device__ constexpr int raw_pos(int r)
+{
+    if (BITS == 2) return (DT == kF16 || r < 3) ? 2 * r : 4;
+    return (r & 1) ? (DT == kF16 ? 4 : 3) : 0;
+}
+
+template <int DT, int BITS>
+__host__ __device__ constexpr float raw_base(int r)
+{
+    return (float)(1 << ((DT == kF16 ? 10 : 7) - raw_pos<DT, BITS>(r)));
+}
+
+template <int DT, int BITS>
+__host__ __device__ constexpr uint32_t raw_magic(int r)
+{
+    // the dtype's bit pattern of raw_base(r), in both halves
+    constexpr int kBias = DT == kF16 ? 15 : 127;
+    constexpr int kMant = DT == kF16 ? 10 : 7;
+    const uint32_t h = (uint32_t)(kBias + kMant - raw_pos<DT, BITS>(r)) << kMant;
+    return h | (h << 16);
+}
+
+template <int DT, int BITS>
+__device__ inline u32x4 raw_step_based(const Span<BITS>& sp, int t, const uint32_t (&magic)[4])
+{
+    constexpr uint32_t kField = BITS == 2 ? 0x00030003u : 0x000f000fu;
+    const uint32_t x = BITS == 2 ? ((t & 1) ? sp.w[t >> 1] >> 8 : sp.w[t >> 1]) : sp.w[t];
+    u32x4 out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        out[r] = and_or(x >> raw_shift<DT, BITS>(r), kField << raw_pos<DT, BITS>(r), magic[r]);
+    }
+    return out;
+}
+
 // Any zero point: (code - zp) * scale in float32, rounded once to the dtype,
 // in the same register order as dequant_step.
 template <int DT, int BITS>

@@ -145,4 +145,9 @@ hipError_t launch_combine(const float* y2, int parts, int64_t part_stride, const
 hipError_t launch_dequant(const ProjArgs& w, int64_t rows, int K, int block_size, int dtype,
                           int32_t* codes_out, void* w_out, hipStream_t s);
 
+// The codes as the decode kernels' raw-code MFMA operands carry them
+// (multi: the streamed kernels' per-register bases, 2/4-bit only).
+hipError_t launch_raw_codes(const uint8_t* codes, int bits, int64_t rows, int K, int dtype,
+                            bool multi, int32_t* codes_out, hipStream_t s);
+
 }  // namespace qmoe

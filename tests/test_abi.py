@@ -177,6 +177,20 @@ def test_dequantize_validation():
         == qm.ERR_INVALID_ARG
 
 
+def test_raw_codes_validation():
+    lib = qm.load_library()
+    p = _proj(bits=3)
+    # 3-bit codes have no multi-base variant; K must be a multiple of 32
+    assert lib.qmoe_raw_codes(ctypes.byref(p), 1, 1, 64, 1, qm.RAW_MULTI_BASE, FAKE, None) \
+        == qm.ERR_UNSUPPORTED
+    assert lib.qmoe_raw_codes(ctypes.byref(p), 1, 1, 48, 1, qm.RAW_SINGLE_BASE, FAKE, None) \
+        == qm.ERR_UNSUPPORTED
+    assert lib.qmoe_raw_codes(ctypes.byref(p), 1, 1, 64, 1, 2, FAKE, None) == qm.ERR_INVALID_ARG
+    assert lib.qmoe_raw_codes(ctypes.byref(p), 1, 1, 64, 3, 0, FAKE, None) == qm.ERR_INVALID_ARG
+    assert lib.qmoe_raw_codes(ctypes.byref(p), 1, 1, 64, 1, 0, None, None) == qm.ERR_INVALID_ARG
+    assert lib.qmoe_raw_codes(None, 1, 1, 64, 1, 0, FAKE, None) == qm.ERR_INVALID_ARG
+
+
 def test_timer_validation():
     lib = qm.load_library()
     assert lib.qmoe_timer_start(7) == qm.ERR_INVALID_ARG

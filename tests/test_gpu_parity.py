@@ -151,6 +151,43 @@ def test_dequant_named_workloads(cfg):
                        spec["block_size"], spec["dtype"])
 
 
+# The decode kernels for block sizes that are multiples of 128 feed the MFMA
+# raw codes (base + code, exact dtype values): the codes they carry must be the
+# oracle's codes bit for bit, for both the single-base routine (m-tile and
+# expert-stationary kernels) and the per-register bases of the streamed kernels.
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("dtype", [1, 2])
+@pytest.mark.parametrize("variant", [0, 1])
+def test_raw_codes_bit_exact(bits, dtype, variant):
+    if variant == qm.RAW_MULTI_BASE and bits == 3:
+        pytest.skip("the streamed kernels take 2- and 4-bit codes only")
+    rng = np.random.default_rng(300 + 10 * bits + dtype + variant)
+    E, N, K = 3, 40, 512
+    codes = rng.integers(0, 256, size=(E, N, K * bits // 8), dtype=np.uint8)
+    scales = np.zeros((E, N, K // 128), dtype=np.uint16)
+    proj = qm.Projection(torch.from_numpy(codes).cuda(), dv.bits_tensor(scales, dtype), None, bits)
+    q = qm.raw_codes(proj, E, N, K, 128, dv.torch_dtype(dtype), variant)
+    q_ref, _ = oracle.dequant(codes, scales, None, K, bits, 128, math.nan, dtype,
+                              want_weights=False)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("variant", [0, 1])
+def test_raw_codes_decode_workload(variant):
+    # the int2 decode layer's own fc1/fc2 codes (two experts each)
+    spec = synth.workload(2)
+    inp = synth.make_inputs(spec, synth.seed_for(2))
+    for name, K in (("fc1", spec["H"]), ("fc2", spec["I"])):
+        codes = inp[name + "_codes"][:2]
+        scales = inp[name + "_scales"][:2]
+        N = codes.shape[1]
+        proj = qm.Projection(torch.from_numpy(codes).cuda(), dv.bits_tensor(scales, 1), None, 2)
+        q = qm.raw_codes(proj, 2, N, K, spec["block_size"], torch.float16, variant)
+        q_ref, _ = oracle.dequant(codes, scales, None, K, 2, spec["block_size"], spec["zpo"], 1,
+                                  want_weights=False)
+        assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
 # ---------------------------------------------------------------- the layer
 def _layer_check(spec, seed, tokens=None, logits=None):
     inp = synth.make_inputs(spec, seed)
@@ -407,16 +444,35 @@ def test_layer_named_workload_full(cfg):
     _layer_check(spec, synth.seed_for(cfg))
 
 
-def test_layer_named_workload_3_sampled():
+def test_layer_named_workload_3_all_tokens():
     spec = synth.workload(3)
-    tokens = np.linspace(0, spec["T"] - 1, 48).astype(np.int64)
-    _layer_check(spec, synth.seed_for(3), tokens=tokens)
+    _layer_check(spec, synth.seed_for(3))
 
 
-def test_layer_named_workload_5_sampled():
+def _tile_edge_tokens(spec, seed, m_tile):
+    """Tokens of the first and last route of every (expert, m-tile) item of
+    the grouped projections, chosen from the oracle's own grouping."""
+    logits = synth.make_logits(spec, seed)
+    ids, _ = oracle.route(logits, spec["k"], spec["normalize"])
+    off, srt, _, _ = oracle.group(ids, spec["E"], m_tile, 1, 1)
+    picks = []
+    for e in range(spec["E"]):
+        for m0 in range(off[e], off[e + 1], m_tile):
+            last = min(m0 + m_tile, off[e + 1]) - 1
+            picks += [srt[m0] // spec["k"], srt[last] // spec["k"]]
+    return np.unique(np.array(picks, dtype=np.int64))
+
+
+def test_layer_named_workload_5_every_tile():
+    # the skewed 4096-token layer runs the 128-row prefill tile: every
+    # (expert, m-tile) item's first and last row is compared, partial last
+    # tiles included, through both fc1 and the K-split fc2
     spec = synth.workload(5)
-    tokens = np.array([0, 1, 777, 2048, 3000, 4095], dtype=np.int64)
-    _layer_check(spec, synth.seed_for(5), tokens=tokens)
+    seed = synth.seed_for(5)
+    tokens = _tile_edge_tokens(spec, seed, 128)
+    _say(f"  comparing {tokens.size} tokens of {spec['T']}")
+    assert tokens.size >= 2 * (spec["T"] * spec["k"] // 128)
+    _layer_check(spec, seed, tokens=tokens)
 
 
 @pytest.mark.parametrize("cfg", [2, 3])
@@ -452,6 +508,8 @@ def test_layer_graph_replay(cfg):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         dv.run_layer(dev, spec, out=out, workspace=ws)
+    ref = oracle.forward(inp, spec)
+    tol = dv.tolerance(ref)
     for _ in range(3):
         out.zero_()
         dv.run_layer(dev, spec, workspace=ws)  # eager work between replays
@@ -459,3 +517,5 @@ def test_layer_graph_replay(cfg):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+        err = float(np.abs(dv.as_f64(out) - ref).max())
+        assert err <= tol, (err, tol)

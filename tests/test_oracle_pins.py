@@ -241,6 +241,47 @@ def test_route_weights_invariants(E, k):
     assert np.all(w_u.sum(axis=1) <= 1.0 + 1e-15)
 
 
+def _f32_bits(u):
+    return struct.unpack("<f", struct.pack("<I", u))[0]
+
+
+def test_route_weights_on_non_finite_rows():
+    # [qmoe.rs, qmoe_route]: the maximum is a running fmaxf over the row, so a
+    # NaN logit never becomes m; the weights are plain IEEE arithmetic on
+    # exp(l - m).  Expected values come from torch float64 softmax over the
+    # selected finite logits, or are NaN where IEEE arithmetic makes them NaN.
+    inf, nan_neg, nan_neg2 = float("inf"), _f32_bits(0xFFC00000), _f32_bits(0xFFFFFFFF)
+    nan_pos = _f32_bits(0x7FC00001)
+    finite_rows = np.array([
+        [1.0, 0.5, nan_neg, 0.2, -inf, 0.1, nan_neg2, -0.3],   # -NaN, -inf unselected
+        [nan_neg, -inf, -2.0, 3.0, -inf, 2.5, nan_neg, -1.0],
+        [-inf, -inf, -inf, 0.0, -inf, -inf, -0.0, -inf],       # finite ones selected first
+    ], dtype=np.float32)
+    for k in (1, 2, 3):
+        ids, w = oracle.route(finite_rows, k, 1)
+        assert np.array_equal(ids, bf.route(finite_rows, k))
+        sel = np.take_along_axis(finite_rows.astype(np.float64), ids.astype(np.int64), 1)
+        assert not np.any(np.isnan(sel)) and np.all(np.isfinite(sel[:, 0]))
+        ref = torch.softmax(torch.from_numpy(sel), dim=1).numpy()
+        assert np.allclose(w, ref, rtol=1e-14, atol=0)
+    # normalize = 0: the denominator sums exp(l - m) over every expert; -inf
+    # terms are 0, and one NaN anywhere makes every weight of the row NaN
+    no_nan = np.array([[1.0, -inf, 0.5, 0.25, -inf, -1.0, 2.0, 0.0]], dtype=np.float32)
+    ids, w = oracle.route(no_nan, 3, 0)
+    ref = torch.softmax(torch.from_numpy(no_nan.astype(np.float64)), dim=1).numpy()
+    assert np.allclose(w, np.take_along_axis(ref, ids.astype(np.int64), 1), rtol=1e-14, atol=0)
+    _, w = oracle.route(finite_rows[:2], 2, 0)
+    assert np.all(np.isnan(w))
+    # a selected +inf or +NaN: exp(inf - inf) and exp(NaN - m) are NaN, and
+    # with normalize = 1 so is the denominator, hence every weight of the row
+    bad = np.array([[0.5, inf, 1.0, -1.0], [nan_pos, 2.0, 1.0, 0.0], [-inf, -inf, -inf, -inf]],
+                   dtype=np.float32)
+    for normalize in (0, 1):
+        ids, w = oracle.route(bad, 2, normalize)
+        assert np.array_equal(ids, bf.route(bad, 2))
+        assert np.all(np.isnan(w)), (normalize, w)
+
+
 def test_route_top1_normalized_weight_is_exactly_one():
     rng = np.random.default_rng(4)
     logits = rng.standard_normal((50, 32)).astype(np.float32)
