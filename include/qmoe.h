@@ -195,6 +195,27 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qmoe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * same arguments and kernels as qmoe_forward without workspace and
+ * workspace_bytes: the workspace is a fixed array of
+ * QMOE_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held until
+ * the process ends.  The call allocates and frees nothing.
+ * Sizes whose qmoe_workspace_size exceeds QMOE_NOALLOC_SCRATCH_BYTES return
+ * QMOE_ERR_WORKSPACE before any launch (64 MiB holds, e.g., 512 tokens of a
+ * hidden = inter = 2048 top-2 layer; use qmoe_forward for larger layers).
+ * Every call on one GPU uses that GPU's array: calls that overlap in time on
+ * one GPU (other streams, other threads) race.  Nothing in the array needs to
+ * start at zero; it keeps the last call's contents.
+ */
+#define QMOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int qmoe_forward_noalloc(const void* hidden, const float* logits, int64_t T, int32_t H, int32_t I,
+                         int32_t E, const qmoe_proj* fc1, const qmoe_proj* fc2,
+                         float zero_point_offset, int32_t block_size, int32_t top_k,
+                         int32_t normalize, int32_t activation, int32_t dtype, void* out,
+                         int32_t* topk_ids_out, float* topk_w_out, void* stream);
+
+/*
  * Test hook: the dequantization of the weight-rounding kernels, written out
  * in full [qmoe.rs, decode_affine_weight: (code - zp) * scale with the code
  * read LSB-first and the zero point from the tensor or the centre; PR 32198,

@@ -35,7 +35,8 @@ RAW_SINGLE_BASE = 0
 RAW_MULTI_BASE = 1
 
 EXPORTED = ("qmoe_last_error", "qmoe_route", "qmoe_worklist_capacity", "qmoe_group",
-            "qmoe_workspace_size", "qmoe_forward", "qmoe_dequantize", "qmoe_raw_codes",
+            "qmoe_workspace_size", "qmoe_forward", "qmoe_forward_noalloc", "qmoe_dequantize",
+            "qmoe_raw_codes",
             "qmoe_timer_start", "qmoe_timer_stop")
 
 
@@ -75,11 +76,15 @@ def load_library(path: str = LIB_PATH):
     lib.qmoe_forward.argtypes = [P, P, i64, i32, i32, i32, ctypes.POINTER(_Proj),
                                  ctypes.POINTER(_Proj), f32, i32, i32, i32, i32, i32, P, P, P, P,
                                  sz, P]
+    lib.qmoe_forward_noalloc.argtypes = [P, P, i64, i32, i32, i32, ctypes.POINTER(_Proj),
+                                         ctypes.POINTER(_Proj), f32, i32, i32, i32, i32, i32, P,
+                                         P, P, P]
     lib.qmoe_dequantize.argtypes = [ctypes.POINTER(_Proj), i32, i32, i32, i32, f32, i32, P, P, P]
     lib.qmoe_raw_codes.argtypes = [ctypes.POINTER(_Proj), i32, i32, i32, i32, i32, P, P]
     lib.qmoe_timer_start.argtypes = [i32]
     lib.qmoe_timer_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
-    for name in ("qmoe_route", "qmoe_group", "qmoe_forward", "qmoe_dequantize", "qmoe_raw_codes",
+    for name in ("qmoe_route", "qmoe_group", "qmoe_forward", "qmoe_forward_noalloc",
+                 "qmoe_dequantize", "qmoe_raw_codes",
                  "qmoe_timer_start", "qmoe_timer_stop"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -228,6 +233,41 @@ def forward(hidden: torch.Tensor, logits: torch.Tensor, fc1: Projection, fc2: Pr
         _ptr(hidden), _ptr(logits), T, H, I, E, ctypes.byref(p1), ctypes.byref(p2),
         float(zero_point_offset), block_size, top_k, normalize, activation, dt, _ptr(out),
         _ptr(ids), _ptr(w), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (out, ids, w) if return_routing else out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def forward_noalloc(hidden: torch.Tensor, logits: torch.Tensor, fc1: Projection,
+                    fc2: Projection, *, top_k: int, block_size: int, normalize: int = 1,
+                    activation: int = ACT_SWIGLU, zero_point_offset: float = math.nan,
+                    out: torch.Tensor, return_routing: bool = False, stream=None):
+    """The QMoE layer through qmoe_forward_noalloc: the library's fixed scratch
+    array serves as workspace and the call allocates nothing on the device
+    (``out`` and, with return_routing, the routing outputs are the caller's)."""
+    dt = dtype_code(hidden.dtype)
+    _dev(hidden, "hidden")
+    T, H = hidden.shape
+    _dev(logits, "logits", torch.float32)
+    if logits.shape[0] != T:
+        raise ValueError("logits rows must equal hidden rows")
+    E = logits.shape[1]
+    for name, proj in (("fc1", fc1), ("fc2", fc2)):
+        if proj.scales.dtype != hidden.dtype:
+            raise ValueError(f"{name}.scales has dtype {proj.scales.dtype}, expected {hidden.dtype}")
+    I = fc2.codes.shape[2] * 8 // fc2.bits
+    p1 = fc1._struct(E, 2 * I, H, block_size, "fc1")
+    p2 = fc2._struct(E, H, I, block_size, "fc2")
+    _dev(out, "out", hidden.dtype, (T, H))
+    ids = w = None
+    if return_routing:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=hidden.device)
+        w = torch.empty((T, top_k), dtype=torch.float32, device=hidden.device)
+    _check(load_library().qmoe_forward_noalloc(
+        _ptr(hidden), _ptr(logits), T, H, I, E, ctypes.byref(p1), ctypes.byref(p2),
+        float(zero_point_offset), block_size, top_k, normalize, activation, dt, _ptr(out),
+        _ptr(ids), _ptr(w), _stream(stream)))
     return (out, ids, w) if return_routing else out
 
 

@@ -53,6 +53,17 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // ---------------------------------------------------------------- kernel timer
 }  // namespace
 
+int qmoe::set_error(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = std::string("qmoe: ") + buf;
+    return code;
+}
+
 qmoe::LaunchEvents& qmoe::launch_events()
 {
     static thread_local LaunchEvents ev;

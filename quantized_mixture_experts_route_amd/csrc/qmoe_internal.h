@@ -17,6 +17,10 @@ struct LaunchEvents {
 };
 LaunchEvents& launch_events();
 
+// Sets the thread's qmoe_last_error() message ("qmoe: " + printf text) and
+// returns `code`.
+int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 template <class Kernel, class... Args>
 inline void launch(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, Args... args)
 {
