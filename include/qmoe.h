@@ -174,6 +174,11 @@ size_t qmoe_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t t
  * bits in {2,3,4} per projection, T*H < 2^32 and T*top_k*I < 2^32 (the
  * projection kernels address their inputs with 32-bit element offsets).
  * T = 0 returns QMOE_OK and enqueues nothing.
+ * Launches: prefill (T*top_k > QMOE_DECODE_MAX_ROUTES) route, group, fc1,
+ * fc2, combine; streamed decode (see qmoe_timer_start) fc1 with routing and
+ * grouping, then fc2 with the combine (its last workgroup per column block
+ * sums the slots, in slot order); other decode layers a routing + m-tile plan,
+ * fc1, fc2 and the combine.
  * Numerics: products accumulate in float32, the activation is rounded to
  * dtype, fc2 outputs stay float32 until the combine.  The prefill kernels
  * (T*top_k > QMOE_DECODE_MAX_ROUTES) and the decode kernels for block sizes
@@ -263,7 +268,9 @@ int qmoe_raw_codes(const qmoe_proj* p, int32_t E, int32_t N, int32_t K, int32_t 
  * elapsed milliseconds and the number of launches timed, and disables the
  * timer.  Stages: 0 route (on the decode path: routing, grouping and the
  * m-tile list in one kernel), 1 group (prefill path only), 2 fc1
- * (+ activation), 3 fc2, 4 combine.
+ * (+ activation), 3 fc2, 4 combine (no launch on the streamed decode path,
+ * T <= 16 and T*top_k <= 64 with E <= min(T*top_k, 64), whose fc2 launch
+ * performs the combine).
  */
 #define QMOE_STAGE_ROUTE 0
 #define QMOE_STAGE_GROUP 1

@@ -116,4 +116,54 @@ __device__ inline float act_value(int act, float gate, float up)
     return act == kGeGLU ? gated<kGeGLU>(gate, up) : gated<kSwiGLU>(gate, up);
 }
 
+// fc2 row values of a decode launch that folds the combine in are written
+// with device-scope (write-through) stores, so another XCD's combining
+// workgroup reads them from the device coherence point without any L2
+// writeback or invalidation.
+__device__ inline void store_y2(float* dst, float v, bool through)
+{
+    if (through) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *dst = v;
+}
+
+// Arrival of one workgroup on fc2 column block n (every thread calls it, with
+// the workgroup's fc2 rows of the block already stored through store_y2, or
+// none at all); the last of `expected` arrivals combines columns
+// [c0, c0 + width) of every token: out[t, c] = RNE_dtype(sum over slots s in
+// order of w[t, s] * y2[t*top_k + s, c]) [qmoe.rs, qmoe_combine:
+// slot-ordered float32 sum, rounded once].  Ordering: each wave waits for its
+// own device-scope stores to complete (s_waitcnt) before the workgroup's
+// arrival increments the counter, and the last arrival reads y2 with
+// device-scope loads after its increment has returned.
+template <int DT>
+__device__ inline void fc2_arrive_combine(const FusedCombine& fc, const float* y2, int H, int top_k,
+                                          int n, int c0, int width, int expected)
+{
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        s_last = __hip_atomic_fetch_add(&fc.counters[n], 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == expected - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    uint16_t* out = reinterpret_cast<uint16_t*>(fc.out);
+    const int items = fc.T * width;
+    for (int i = threadIdx.x; i < items; i += blockDim.x) {
+        const int t = i / width;
+        const int c = c0 + (i - t * width);
+        float sum = 0.0f;
+        for (int s = 0; s < top_k; ++s) {
+            const int64_t r = (int64_t)t * top_k + s;
+            sum += fc.weights[r] *
+                   __hip_atomic_load(y2 + r * H + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        out[(int64_t)t * H + c] = Dt<DT>::from_float(sum);
+    }
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(&fc.counters[n], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 }  // namespace qmoe

@@ -253,7 +253,7 @@ __device__ inline void reduce_store(uint32_t* lds, const f32x4 (&acc)[NB], const
             float v = 0.f;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) v += red[(w * MTR + m) * (kCols + 1) + h];
-            p.y2[(int64_t)out_row(m) * p.N + col0 + h] = v;
+            store_y2(&p.y2[(int64_t)out_row(m) * p.N + col0 + h], v, p.fused.counters != nullptr);
         }
     }
     __syncthreads();  // lds is free again
@@ -339,6 +339,9 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(ProjLaunch p,
         reduce_store<DT, FC1, NB, kDecodeMT>(lds, acc, p, rows, col0, tid, wave, g, c, [&](int m) {
             return FC1 ? row0 + m : it[kDecodeTileRoutes + m];
         });
+        if constexpr (!FC1) {  // one arrival per m-tile on column block n
+            if (p.fused.counters) fc2_arrive_combine<DT>(p.fused, p.y2, p.N, p.top_k, n, col0, kCols, n_items / nt);
+        }
     }
 }
 
@@ -379,7 +382,14 @@ __global__ __launch_bounds__(kThreads, 4) void decode_rows_kernel(ProjLaunch p,
     const int nt = p.N / kRowsItem;
     const int tile = blockIdx.x / nt;
     const int n = blockIdx.x - tile * nt;
-    if (tile >= *n_tiles_ptr) return;  // whole workgroup
+    if (tile >= *n_tiles_ptr) {  // whole workgroup; fc2 still arrives on its column block
+        if constexpr (!FC1) {
+            if (p.fused.counters) {
+                fc2_arrive_combine<DT>(p.fused, p.y2, p.N, p.top_k, n, n * kRowsItem, kRowsItem, gridDim.x / nt);
+            }
+        }
+        return;
+    }
     const int32_t* it = tiles + (int64_t)kDecodeTileInts * tile;
     const int e = it[0];
     const int row0 = it[1];
@@ -481,8 +491,14 @@ __global__ __launch_bounds__(kThreads, 4) void decode_rows_kernel(ProjLaunch p,
                 out[n * (kRowsItem / 2) + 8 * wave + c] = Dt<DT>::from_float(act_value<DT>(p.act, sum[i], up));
             }
         } else {
-            if (m < rows) p.y2[(int64_t)y2_row[i] * p.N + n * kRowsItem + kRowsWave * wave + c] = sum[i];
+            if (m < rows) {
+                store_y2(&p.y2[(int64_t)y2_row[i] * p.N + n * kRowsItem + kRowsWave * wave + c], sum[i],
+                         p.fused.counters != nullptr);
+            }
         }
+    }
+    if constexpr (!FC1) {
+        if (p.fused.counters) fc2_arrive_combine<DT>(p.fused, p.y2, p.N, p.top_k, n, n * kRowsItem, kRowsItem, gridDim.x / nt);
     }
 }
 
@@ -577,6 +593,9 @@ __global__ __launch_bounds__(kThreads, 4) void decode_expert_kernel(ProjLaunch p
     if constexpr (FC1) {
         const int R = q.T * p.top_k;
         const bool writer = blockIdx.x == 0;
+        if (writer && tid < q.n_counters) {  // fc2's column-block counters start at zero
+            __hip_atomic_store(&q.counters[tid], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
 #pragma unroll
         for (int j = 0; j < kTokensPerWave; ++j) {
             const int t = wave + kWaves * j;
@@ -626,7 +645,12 @@ __global__ __launch_bounds__(kThreads, 4) void decode_expert_kernel(ProjLaunch p
         count = s_count[0] + s_count[1];
         first = s_count[2] + s_count[3];
     }
-    if (count == 0) return;  // whole workgroup; the weight loads drain on their own
+    if (count == 0) {  // whole workgroup; the weight loads drain on their own
+        if constexpr (!FC1) {
+            if (p.fused.counters) fc2_arrive_combine<DT>(p.fused, p.y2, p.N, p.top_k, n, col0, kCols, q.E);
+        }
+        return;
+    }
 
     // 3) the expert's rows, kExpertRows at a time, against the same weights
     for (int m0 = 0; m0 < count; m0 += kExpertRows) {
@@ -675,6 +699,9 @@ __global__ __launch_bounds__(kThreads, 4) void decode_expert_kernel(ProjLaunch p
         reduce_store<DT, FC1, NB, kExpertRows>(lds, acc, p, rows, col0, tid, wave, g, c, [&](int m) {
             return FC1 ? first + m0 + m : q.sorted[first + m0 + m];
         });
+    }
+    if constexpr (!FC1) {
+        if (p.fused.counters) fc2_arrive_combine<DT>(p.fused, p.y2, p.N, p.top_k, n, col0, kCols, q.E);
     }
 }
 

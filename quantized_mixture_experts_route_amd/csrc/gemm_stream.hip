@@ -264,7 +264,10 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
     } else {
         first = q.offsets[e];
         count = q.offsets[e + 1] - first;
-        if (count == 0) return;
+        if (count == 0) {  // no rows of this expert: arrive on the column block only
+            if (p.fused.counters) fc2_arrive_combine<DT>(p.fused, y2, p.N, p.top_k, n, n * kRowsWG, kRowsWG, q.E);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) y2_row[i] = q.sorted[first + min(4 * g + i, count - 1)];
     }
@@ -326,6 +329,10 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
     if constexpr (FC1) {
         const int R = q.T * p.top_k;
         const bool writer = blockIdx.x == 0;
+        // the fc2 launch's column-block counters start at zero
+        if (writer && tid < q.n_counters) {
+            __hip_atomic_store(&q.counters[tid], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
 #pragma unroll
         for (int j = 0; j < kTokW; ++j) {
             const int t = wave + kWavesS * j;
@@ -429,15 +436,16 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
         magic);
 
     // 8) epilogue: lane (g, c) holds MFMA rows 4g..4g+3 of column c
+    bool stores = true;
     if constexpr (KS == 2) {  // the second K share hands its sums to the first
         f32x4* r4 = reinterpret_cast<f32x4*>(red) + rb * kWave + lane;
         if (kp == 1) *r4 = sum;
         __syncthreads();
-        if (kp == 1) return;
-        sum += *r4;
+        stores = kp == 0;
+        if (stores) sum += *r4;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4 && stores; ++i) {
         const int m = 4 * g + i;
         if constexpr (FC1) {
             const float up = dpp_f32<kDppRor8>(sum[i]);  // column c + 8: the up row of column c
@@ -447,8 +455,11 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
                 out[col0 + c] = Dt<DT>::from_float(act_value<DT>(act, sum[i], up));
             }
         } else {
-            if (m < count) y2[(int64_t)y2_row[i] * p.N + col0 + c] = sum[i];
+            if (m < count) store_y2(&y2[(int64_t)y2_row[i] * p.N + col0 + c], sum[i], p.fused.counters != nullptr);
         }
+    }
+    if constexpr (!FC1) {
+        if (p.fused.counters) fc2_arrive_combine<DT>(p.fused, y2, p.N, p.top_k, n, n * kRowsWG, kRowsWG, q.E);
     }
 }
 

@@ -29,7 +29,8 @@ template <int EPL>
 __global__ __launch_bounds__(kThreads) void decode_plan_kernel(
     const float* __restrict__ logits, int T, int E, int top_k, int normalize,
     float* __restrict__ weights, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
-    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles)
+    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles, int32_t* __restrict__ counters,
+    int n_counters)
 {
     __shared__ __attribute__((aligned(16))) int s_e[kDecodeMaxRoutes];  // expert of route r
     __shared__ int s_route[kDecodeMaxRoutes];  // route at sorted position p
@@ -45,6 +46,10 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(
     // routes past R keep a sentinel above every expert, so the rank loop
     // reads the whole table without a bound
     if (tid >= R && tid < kDecodeMaxRoutes) s_e[tid] = INT32_MAX;
+    // the fc2 launch's column-block counters (combine folded into fc2) start at zero
+    for (int i = tid; i < n_counters; i += kThreads) {
+        __hip_atomic_store(&counters[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // 1) routing
     for (int t = wave; t < T; t += kWaves) {
@@ -125,10 +130,11 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(
 
 template <int EPL>
 hipError_t launch_epl(const float* logits, int T, int E, int top_k, int normalize, float* weights,
-                  int32_t* ids_out, float* w_out, int32_t* tiles, int32_t* n_tiles, hipStream_t s)
+                  int32_t* ids_out, float* w_out, int32_t* tiles, int32_t* n_tiles,
+                  int32_t* counters, int n_counters, hipStream_t s)
 {
     launch(decode_plan_kernel<EPL>, dim3(1), dim3(kThreads), s, logits, T, E, top_k,
-                       normalize, weights, ids_out, w_out, tiles, n_tiles);
+                       normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters);
     return hipGetLastError();
 }
 
@@ -136,15 +142,15 @@ hipError_t launch_epl(const float* logits, int T, int E, int top_k, int normaliz
 
 hipError_t launch_decode_plan(const float* logits, int T, int E, int top_k, int normalize,
                               float* weights, int32_t* ids_out, float* w_out, int32_t* tiles,
-                              int32_t* n_tiles, hipStream_t s)
+                              int32_t* n_tiles, int32_t* counters, int n_counters, hipStream_t s)
 {
     if (T < 1 || T * top_k > kDecodeMaxRoutes) return hipErrorInvalidValue;
     const int epl = (E + kWave - 1) / kWave;
-    if (epl <= 1) return launch_epl<1>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
-    if (epl <= 2) return launch_epl<2>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
-    if (epl <= 4) return launch_epl<4>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
-    if (epl <= 8) return launch_epl<8>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
-    return launch_epl<16>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, s);
+    if (epl <= 1) return launch_epl<1>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, s);
+    if (epl <= 2) return launch_epl<2>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, s);
+    if (epl <= 4) return launch_epl<4>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, s);
+    if (epl <= 8) return launch_epl<8>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, s);
+    return launch_epl<16>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, s);
 }
 
 }  // namespace qmoe

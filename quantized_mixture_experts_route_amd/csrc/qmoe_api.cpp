@@ -111,8 +111,15 @@ struct Layout {
     int nt1, nt2;       // n-tiles of fc1 (activation columns) and fc2 (hidden columns)
     int64_t cap1, cap2;  // work-list capacities
     int64_t m_tiles;     // m-tile capacity
-    size_t ids, w, offsets, sorted, wl1, n1, wl2, n2, act, y2, total;
+    int n_counters;      // decode: fc2 column blocks with a combine counter (0: separate combine)
+    size_t ids, w, offsets, sorted, wl1, n1, wl2, n2, act, y2, counters, total;
 };
+
+// Decode fc2 launches fold the combine in when every fc2 column block (at
+// most H/32 of them, the narrowest decode fc2 block) has a counter that one
+// thread of the zeroing workgroup can clear.
+constexpr int kFusedCounterCols = 32;
+constexpr int kMaxFusedCounters = 512;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -199,6 +206,9 @@ bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L,
     }
     L->act = take((size_t)act_bytes);
     L->y2 = take((size_t)y2_bytes);
+    const int64_t blocks = ceil_div(H, kFusedCounterCols);
+    L->n_counters = L->decode && blocks <= kMaxFusedCounters ? (int)blocks : 0;
+    L->counters = take((size_t)L->n_counters * 4);
     L->total = off;
     return true;
 }
@@ -406,6 +416,8 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     int32_t* n2 = reinterpret_cast<int32_t*>(ws + L.n2);
     void* act = ws + L.act;
     float* y2 = reinterpret_cast<float*>(ws + L.y2);
+    int32_t* counters = L.n_counters ? reinterpret_cast<int32_t*>(ws + L.counters) : nullptr;
+    int n_counters = L.n_counters;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
 
@@ -422,7 +434,17 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
                              qmoe::stream_fits(w2, I, H, block_size, false);
     const bool expert_mode = !stream_mode && L.decode && E <= 64 && E <= R && H <= 2048 &&
                              I <= 2048 && fc1->bits == 2 && fc1->zero_points == nullptr;
-    qmoe::DecodePlan plan{logits, (int)T, E, normalize, w, topk_ids_out, topk_w_out, offsets, sorted};
+    // The combine folds into fc2 on the streamed path only: there a column
+    // block's few expert workgroups finish together; the m-tile and
+    // expert-stationary paths have many more arrivals per block and the
+    // combining workgroup becomes a serial tail (measured slower than the
+    // separate combine launch).
+    if (!stream_mode) {
+        counters = nullptr;
+        n_counters = 0;
+    }
+    qmoe::DecodePlan plan{logits, (int)T, E, normalize, w, topk_ids_out, topk_w_out, offsets, sorted,
+                          counters, n_counters};
     const qmoe::DecodePlan* dplan = expert_mode ? &plan : nullptr;
     // Row-block kernels for the m-tile list: an expert has at most one route
     // per token, so a tile holds at most min(T, 16) rows.
@@ -433,7 +455,7 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     if (L.decode && !expert_mode && !stream_mode) {  // routing, grouping and the m-tile list in one launch
         timer_begin(QMOE_STAGE_ROUTE, s);
         e = qmoe::launch_decode_plan(logits, (int)T, E, top_k, normalize, w, topk_ids_out,
-                                     topk_w_out, wl1, n1, s);
+                                     topk_w_out, wl1, n1, counters, n_counters, s);
         timer_end(QMOE_STAGE_ROUTE, s);
         if (e != hipSuccess) return hip_fail(e, "decode plan launch");
     } else if (!L.decode) {
@@ -490,6 +512,7 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     p2.y2 = y2;
     p2.k_split = k_split;
     p2.part_stride = R * (int64_t)H;
+    p2.fused = qmoe::FusedCombine{counters, w, out, (int)T};  // decode: fc2 combines (counters set)
     timer_begin(QMOE_STAGE_FC2, s);
     e = stream_mode ? qmoe::launch_fc2_stream(p2, plan, dtype, s)
         : rows2     ? qmoe::launch_rows_decode(p2, false, max_rows, dtype, s)
@@ -498,10 +521,12 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     timer_end(QMOE_STAGE_FC2, s);
     if (e != hipSuccess) return hip_fail(e, "fc2 launch");
 
-    timer_begin(QMOE_STAGE_COMBINE, s);
-    e = qmoe::launch_combine(y2, k_split, R * (int64_t)H, w, T, H, top_k, out, dtype, s);
-    timer_end(QMOE_STAGE_COMBINE, s);
-    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    if (counters == nullptr) {  // prefill (and very wide decode layers): the combine launch
+        timer_begin(QMOE_STAGE_COMBINE, s);
+        e = qmoe::launch_combine(y2, k_split, R * (int64_t)H, w, T, H, top_k, out, dtype, s);
+        timer_end(QMOE_STAGE_COMBINE, s);
+        if (e != hipSuccess) return hip_fail(e, "combine launch");
+    }
 
     if (!L.decode && topk_ids_out) {
         e = hipMemcpyAsync(topk_ids_out, ids, (size_t)R * 4, hipMemcpyDeviceToDevice, s);

@@ -71,6 +71,18 @@ struct ProjArgs {
     int fast;           // every zero point is a multiple of 1/2 below 256: fast dequant
 };
 
+// The combine folded into a decode fc2 launch: every workgroup that writes
+// fc2 rows of column block n arrives once on counters[n] (zeroed by the fc1 or
+// plan launch before fc2 starts); the last to arrive sums, for the block's
+// columns, each token's slots in slot order (the combine's arithmetic) and
+// resets counters[n] to 0.  counters == nullptr: the separate combine runs.
+struct FusedCombine {
+    int32_t* counters;     // [column blocks of fc2]
+    const float* weights;  // [T * top_k] routing weights
+    void* out;             // dtype [T, H]
+    int T;
+};
+
 // One grouped projection over a work-list.
 struct ProjLaunch {
     const void* a;            // fc1: hidden [T, K]; fc2: activations [R, K] in sorted order
@@ -91,6 +103,7 @@ struct ProjLaunch {
     float* y2;                // fc2: float32 [R, H] by route id (k_split parts)
     int k_split;              // prefill fc2: K parts (1, 2 or 4), each a work-list column block
     int64_t part_stride;      // prefill fc2: floats between the parts of y2
+    FusedCombine fused;       // decode fc2: the combine folded in (counters nullable)
 };
 
 // Routing inputs and outputs of the expert-stationary decode kernels: fc1
@@ -105,6 +118,8 @@ struct DecodePlan {
     float* w_out;         // nullable [R]
     int32_t* offsets;     // [E+1] expert offsets into the sorted routes
     int32_t* sorted;      // [R] route ids grouped by expert, ascending
+    int32_t* counters;    // nullable [n_counters]: zeroed by fc1's first workgroup
+    int n_counters;
 };
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int top_k, int normalize,
@@ -118,7 +133,7 @@ hipError_t launch_group(const int32_t* ids, int R, int E, int m_tile, int nt1, i
 // kDecodeMaxRoutes).  ids_out / w_out may be NULL.
 hipError_t launch_decode_plan(const float* logits, int T, int E, int top_k, int normalize,
                               float* weights, int32_t* ids_out, float* w_out, int32_t* tiles,
-                              int32_t* n_tiles, hipStream_t s);
+                              int32_t* n_tiles, int32_t* counters, int n_counters, hipStream_t s);
 
 hipError_t launch_fc1_prefill(const ProjLaunch& p, int dtype, hipStream_t s);
 hipError_t launch_fc2_prefill(const ProjLaunch& p, int dtype, hipStream_t s);
