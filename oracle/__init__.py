@@ -51,6 +51,7 @@ def _load():
                                    P, P, P, i32, P, P, P, i32,
                                    f64, i32, i32, i32, i32, i32, P, i64, P]
     lib.oracle_group.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, i64, P]
+    lib.oracle_router_logits.argtypes = [P, P, i64, i32, i32, i32, P]
     _lib = lib
     return lib
 
@@ -73,6 +74,18 @@ def widen(bits: np.ndarray, dtype: int) -> np.ndarray:
 
 def route_key(x: float) -> int:
     return int(_load().oracle_route_key(float(np.float32(x))))
+
+
+def router_logits(hidden: np.ndarray, weight: np.ndarray, dtype: int) -> np.ndarray:
+    """Router logits (float64 [T, E]) = hidden [T, H] @ weight[E, H]^T, both fp16/bf16 bit patterns."""
+    hidden = _c(hidden, np.uint16)
+    weight = _c(weight, np.uint16)
+    T, H = hidden.shape
+    E = weight.shape[0]
+    assert weight.shape[1] == H
+    out = np.empty((T, E), dtype=np.float64)
+    _load().oracle_router_logits(_ptr(hidden), _ptr(weight), T, H, E, dtype, _ptr(out))
+    return out
 
 
 def route(logits: np.ndarray, top_k: int, normalize: int):

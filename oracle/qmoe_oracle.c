@@ -167,6 +167,28 @@ void oracle_route(const float* logits, int64_t T, int32_t E, int32_t top_k, int3
 }
 
 /* ------------------------------------------------------------------ */
+/* Router projection  [gemm_quant_moe.rs, moe_gate_topk_fused: the gate   */
+/* logits of a token are its input row times the transposed gate weight   */
+/* matrix, one logit per expert; ferrum moe.rs, the router GEMM before    */
+/* routing].  logits[t, e] = sum_h x[t, h] * w[e, h], exact in double     */
+/* from the dtype values (w is [E, H] row-major).                         */
+/* ------------------------------------------------------------------ */
+void oracle_router_logits(const uint16_t* hidden, const uint16_t* weight, int64_t T, int32_t H,
+                          int32_t E, int32_t dtype, double* logits)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int32_t h = 0; h < H; ++h) {
+                acc += widen(hidden[t * H + h], dtype) * widen(weight[(int64_t)e * H + h], dtype);
+            }
+            logits[t * E + e] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Codes, zero points, dequantization                                   */
 /* [qmoe.rs, decode_affine_weight]; [PR 32198, zero_point_offset];      */
 /* [PR 33569, 24-bit 8-code INT3 groups]                                */

@@ -154,6 +154,20 @@ def make_inputs(spec: dict, seed: int) -> dict:
     return out
 
 
+def make_router_weights(E: int, H: int, dtype: int, seed: int) -> np.ndarray:
+    """Router (gate) weight bit patterns [E, H]: N(0, 1/H) values rounded to the dtype,
+    so that the logits of N(0, 1) hidden rows are about N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((E, H), dtype=np.float32) * np.float32(1.0 / math.sqrt(H))
+    return np.ascontiguousarray(_to_dtype_bits(w, dtype))
+
+
+def make_hidden(T: int, H: int, dtype: int, seed: int) -> np.ndarray:
+    """Hidden-state bit patterns [T, H]: N(0, 1) rounded to the dtype."""
+    rng = np.random.default_rng(seed)
+    return np.ascontiguousarray(_to_dtype_bits(rng.standard_normal((T, H), dtype=np.float32), dtype))
+
+
 def seed_for(i: int) -> int:
     """Default seed of named workload ``i``."""
     return 1000 + i

@@ -289,6 +289,36 @@ def test_route_top1_normalized_weight_is_exactly_one():
     assert np.all(w == 1.0)
 
 
+# ---------------------------------------------------------------- router projection
+@pytest.mark.parametrize("dtype", [1, 2])
+def test_router_logits_match_torch_float64_linear(dtype):
+    # the oracle's plain loop against torch's float64 matmul on the same values
+    T, H, E = 7, 96, 13
+    x = synth.make_hidden(T, H, dtype, 5)
+    w = synth.make_router_weights(E, H, dtype, 6)
+    got = oracle.router_logits(x, w, dtype)
+    ref = F.linear(torch.from_numpy(bf.widen(x, dtype)), torch.from_numpy(bf.widen(w, dtype))).numpy()
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-15)
+
+
+def test_router_logits_one_hot_rows_pick_hidden_elements():
+    # weight row e = one-hot at h_e with value 1: logit e is exactly x[t, h_e];
+    # a row of twos doubles the sum of the row (exact: small integers)
+    T, H, E = 4, 64, 5
+    x16 = (np.arange(T * H, dtype=np.float32).reshape(T, H) % 17 - 8).astype(np.float16)
+    x = x16.view(np.uint16)
+    w = np.zeros((E, H), dtype=np.float16)
+    picks = [0, 7, 31, 63]
+    for e, h in enumerate(picks):
+        w[e, h] = 1.0
+    w[4, :] = 2.0
+    got = oracle.router_logits(x, w.view(np.uint16), 1)
+    x64 = x16.astype(np.float64)
+    assert np.array_equal(got[:, :4], x64[:, picks])
+    assert np.array_equal(got[:, 4], 2.0 * x64.sum(axis=1))
+    assert np.array_equal(oracle.router_logits(np.zeros_like(x), w.view(np.uint16), 1), np.zeros((T, E)))
+
+
 # ---------------------------------------------------------------- grouping
 @pytest.mark.parametrize("E,R,m_tile,n_tile,N", [(8, 64, 16, 64, 200), (512, 60, 16, 32, 64),
                                                  (3, 1, 128, 128, 128), (8, 1000, 128, 256, 4096),
