@@ -111,6 +111,24 @@ const char* qmoe_last_error(void);
 int qmoe_route(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t normalize,
                int32_t* topk_ids, float* topk_weights, void* stream);
 
+/*
+ * Router projection fused with top-k routing, one launch
+ * [gemm_quant_moe.rs, moe_gate_topk_fused: gate logits = input row times the
+ * transposed gate weight, then the top-k expert indices and weights of those
+ * logits; moe.rs, the router GEMM before routing].
+ *   hidden        dtype [T, H] (16-byte aligned)
+ *   gate_weight   dtype [E, H] row-major (16-byte aligned): one row per expert
+ *   logits_out    NULL or float32 [T, E] out: sum_h hidden[t,h] * gate[e,h],
+ *                 products and sums in float32 (the values routed on; they can
+ *                 be passed to qmoe_forward as its logits)
+ *   topk_ids, topk_weights   as qmoe_route computes them from those logits
+ * Requires 1 <= E <= 1024, 1 <= top_k <= E, H a multiple of 32 (else
+ * QMOE_ERR_UNSUPPORTED).  T = 0 returns QMOE_OK and enqueues nothing.
+ */
+int qmoe_router(const void* hidden, const void* gate_weight, int64_t T, int32_t H, int32_t E,
+                int32_t dtype, int32_t top_k, int32_t normalize, float* logits_out,
+                int32_t* topk_ids, float* topk_weights, void* stream);
+
 /* Work-list capacity (items) that always suffices for qmoe_group with these
  * arguments: (ceil(R/m_tile) + min(E, R)) * ceil(N/n_tile), R = T*top_k
  * [gemm_quant_moe.rs, moe_build_tile_worklist: one item per m-tile and

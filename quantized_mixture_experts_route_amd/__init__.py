@@ -34,7 +34,7 @@ STAGE_ROUTE, STAGE_GROUP, STAGE_FC1, STAGE_FC2, STAGE_COMBINE = range(5)
 RAW_SINGLE_BASE = 0
 RAW_MULTI_BASE = 1
 
-EXPORTED = ("qmoe_last_error", "qmoe_route", "qmoe_worklist_capacity", "qmoe_group",
+EXPORTED = ("qmoe_last_error", "qmoe_route", "qmoe_router", "qmoe_worklist_capacity", "qmoe_group",
             "qmoe_workspace_size", "qmoe_forward", "qmoe_forward_noalloc", "qmoe_dequantize",
             "qmoe_raw_codes",
             "qmoe_timer_start", "qmoe_timer_stop")
@@ -68,6 +68,7 @@ def load_library(path: str = LIB_PATH):
     lib.qmoe_last_error.restype = ctypes.c_char_p
     lib.qmoe_last_error.argtypes = []
     lib.qmoe_route.argtypes = [P, i64, i32, i32, i32, P, P, P]
+    lib.qmoe_router.argtypes = [P, P, i64, i32, i32, i32, i32, i32, P, P, P, P]
     lib.qmoe_worklist_capacity.argtypes = [i64, i32, i32, i32, i32, i32]
     lib.qmoe_worklist_capacity.restype = i64
     lib.qmoe_group.argtypes = [P, i64, i32, i32, i32, i32, i32, P, P, P, i64, P, P]
@@ -83,7 +84,7 @@ def load_library(path: str = LIB_PATH):
     lib.qmoe_raw_codes.argtypes = [ctypes.POINTER(_Proj), i32, i32, i32, i32, i32, P, P]
     lib.qmoe_timer_start.argtypes = [i32]
     lib.qmoe_timer_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
-    for name in ("qmoe_route", "qmoe_group", "qmoe_forward", "qmoe_forward_noalloc",
+    for name in ("qmoe_route", "qmoe_router", "qmoe_group", "qmoe_forward", "qmoe_forward_noalloc",
                  "qmoe_dequantize", "qmoe_raw_codes",
                  "qmoe_timer_start", "qmoe_timer_stop"):
         getattr(lib, name).restype = ctypes.c_int
@@ -164,6 +165,25 @@ def route(logits: torch.Tensor, top_k: int, normalize: int = 1, stream=None):
     _check(load_library().qmoe_route(_ptr(logits), T, E, top_k, normalize, _ptr(ids), _ptr(w),
                                      _stream(stream)))
     return ids, w
+
+
+def router(hidden: torch.Tensor, gate_weight: torch.Tensor, top_k: int, normalize: int = 1,
+           want_logits: bool = True, stream=None):
+    """Router projection + top-k in one launch: (logits float32 [T, E] or None,
+    ids int32 [T, k], weights float32 [T, k]); gate_weight is [E, H] in hidden's dtype."""
+    dt = dtype_code(hidden.dtype)
+    _dev(hidden, "hidden")
+    T, H = hidden.shape
+    E = gate_weight.shape[0]
+    _dev(gate_weight, "gate_weight", hidden.dtype, (E, H))
+    dev = hidden.device
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    _check(load_library().qmoe_router(_ptr(hidden), _ptr(gate_weight), T, H, E, dt, top_k,
+                                      normalize, _ptr(logits), _ptr(ids), _ptr(w),
+                                      _stream(stream)))
+    return logits, ids, w
 
 
 def worklist_capacity(T, top_k, E, m_tile, n_tile, N) -> int:

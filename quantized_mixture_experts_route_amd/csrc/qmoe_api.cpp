@@ -291,6 +291,37 @@ int qmoe_route(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t
     return e == hipSuccess ? ok() : hip_fail(e, "route launch");
 }
 
+int qmoe_router(const void* hidden, const void* gate_weight, int64_t T, int32_t H, int32_t E,
+                int32_t dtype, int32_t top_k, int32_t normalize, float* logits_out,
+                int32_t* topk_ids, float* topk_weights, void* stream)
+{
+    if (T < 0) return fail(QMOE_ERR_INVALID_ARG, "T=%lld < 0", (long long)T);
+    if (E < 1 || E > 1024) return fail(QMOE_ERR_INVALID_ARG, "E=%d outside [1, 1024]", E);
+    if (top_k < 1 || top_k > E) return fail(QMOE_ERR_INVALID_ARG, "top_k=%d outside [1, E=%d]", top_k, E);
+    if (normalize != 0 && normalize != 1) return fail(QMOE_ERR_INVALID_ARG, "normalize must be 0 or 1");
+    if (dtype != QMOE_DTYPE_F16 && dtype != QMOE_DTYPE_BF16) {
+        return fail(QMOE_ERR_INVALID_ARG, "dtype=%d is neither F16 (1) nor BF16 (2)", dtype);
+    }
+    if (H < 1) return fail(QMOE_ERR_INVALID_ARG, "H=%d must be >= 1", H);
+    if (H % 32) return fail(QMOE_ERR_UNSUPPORTED, "H=%d must be a multiple of 32", H);
+    int64_t n;
+    if (!mul_ok(T, E, &n) || !mul_ok(T, H, &n) || !mul_ok(T, top_k, &n)) {
+        return fail(QMOE_ERR_INVALID_ARG, "sizes overflow");
+    }
+    if (T == 0) return ok();
+    if (!hidden || !gate_weight || !topk_ids || !topk_weights) return fail(QMOE_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned(hidden, 16) || !aligned(gate_weight, 16) || !aligned(topk_ids, 4) ||
+        !aligned(topk_weights, 4) || (logits_out && !aligned(logits_out, 4))) {
+        return fail(QMOE_ERR_INVALID_ARG, "hidden/gate_weight must be 16-byte and outputs 4-byte aligned");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    timer_begin(QMOE_STAGE_ROUTE, s);
+    const hipError_t e = qmoe::launch_router(hidden, gate_weight, T, H, E, top_k, normalize, dtype,
+                                             logits_out, topk_ids, topk_weights, s);
+    timer_end(QMOE_STAGE_ROUTE, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "router launch");
+}
+
 int64_t qmoe_worklist_capacity(int64_t T, int32_t top_k, int32_t E, int32_t m_tile,
                                int32_t n_tile, int32_t N)
 {

@@ -125,6 +125,12 @@ struct DecodePlan {
 hipError_t launch_route(const float* logits, int64_t T, int E, int top_k, int normalize,
                         int32_t* ids, float* weights, hipStream_t s);
 
+// Router projection + top-k (router.hip): logits = hidden @ gate_weight^T in
+// float32 on the matrix cores, then route_values on them.
+hipError_t launch_router(const void* hidden, const void* gate_weight, int64_t T, int H, int E,
+                         int top_k, int normalize, int dtype, float* logits_out, int32_t* ids,
+                         float* weights, hipStream_t s);
+
 hipError_t launch_group(const int32_t* ids, int R, int E, int m_tile, int nt1, int32_t* offsets,
                         int32_t* sorted, int32_t* wl1, int64_t cap1, int32_t* n1, int nt2,
                         int32_t* wl2, int64_t cap2, int32_t* n2, hipStream_t s);

@@ -191,6 +191,28 @@ def test_raw_codes_validation():
     assert lib.qmoe_raw_codes(None, 1, 1, 64, 1, 0, FAKE, None) == qm.ERR_INVALID_ARG
 
 
+def test_router_validation():
+    lib = qm.load_library()
+    args = [FAKE, FAKE, 4, 256, 8, 1, 2, 1, None, FAKE, FAKE, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["hidden", "gate", "T", "H", "E", "dtype", "k", "norm", "logits", "ids", "w", "s"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return lib.qmoe_router(*a)
+
+    assert call(H=240) == qm.ERR_UNSUPPORTED       # not a multiple of 32
+    assert call(E=0) == qm.ERR_INVALID_ARG
+    assert call(E=1025) == qm.ERR_INVALID_ARG
+    assert call(k=9) == qm.ERR_INVALID_ARG
+    assert call(dtype=3) == qm.ERR_INVALID_ARG
+    assert call(norm=2) == qm.ERR_INVALID_ARG
+    assert call(hidden=None) == qm.ERR_INVALID_ARG
+    assert call(gate=FAKE + 8) == qm.ERR_INVALID_ARG  # 16-byte alignment
+    assert call(T=0, hidden=None) == qm.OK           # nothing to do
+
+
 def test_timer_validation():
     lib = qm.load_library()
     assert lib.qmoe_timer_start(7) == qm.ERR_INVALID_ARG
