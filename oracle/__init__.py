@@ -52,6 +52,8 @@ def _load():
                                    f64, i32, i32, i32, i32, i32, P, i64, P]
     lib.oracle_group.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, i64, P]
     lib.oracle_router_logits.argtypes = [P, P, i64, i32, i32, i32, P]
+    lib.oracle_shared_expert.argtypes = [P, i64, i32, i32, P, P, P, i32, P, P, P, i32,
+                                         f64, i32, i32, i32, P, P, i64, P]
     _lib = lib
     return lib
 
@@ -147,4 +149,25 @@ def forward(inp: dict, spec: dict, tokens=None) -> np.ndarray:
         _ptr(arrs["c2"]), _ptr(arrs["s2"]), _ptr(arrs["z2"]), spec["fc2_bits"],
         float(spec["zpo"]), spec["block_size"], spec["k"], spec["normalize"], spec["act"],
         spec["dtype"], _ptr(tokens), tokens.size, _ptr(out))
+    return out
+
+
+def shared_expert(inp: dict, shared: dict, spec: dict, tokens=None) -> np.ndarray:
+    """The shared expert's gated contribution (float64 [n_tokens, H]) for the given tokens:
+    sigmoid(x . gate) * shared_fc2(act(shared_fc1(x)))."""
+    T, H = spec["T"], spec["H"]
+    Is = shared["I"]
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int64)
+    tokens = _c(tokens, np.int64)
+    out = np.empty((tokens.size, H), dtype=np.float64)
+    a = dict(hidden=_c(inp["hidden"], np.uint16), c1=_c(shared["fc1_codes"], np.uint8),
+             s1=_c(shared["fc1_scales"], np.uint16), z1=_c(shared["fc1_zp"], np.uint8),
+             c2=_c(shared["fc2_codes"], np.uint8), s2=_c(shared["fc2_scales"], np.uint16),
+             z2=_c(shared["fc2_zp"], np.uint8), g=_c(shared["gate"], np.uint16))
+    _load().oracle_shared_expert(
+        _ptr(a["hidden"]), T, H, Is, _ptr(a["c1"]), _ptr(a["s1"]), _ptr(a["z1"]), spec["fc1_bits"],
+        _ptr(a["c2"]), _ptr(a["s2"]), _ptr(a["z2"]), spec["fc2_bits"], float(spec["zpo"]),
+        spec["block_size"], spec["act"], spec["dtype"], _ptr(a["g"]), _ptr(tokens), tokens.size,
+        _ptr(out))
     return out

@@ -350,6 +350,77 @@ void oracle_forward(const uint16_t* hidden, const float* logits, int64_t T, int3
 }
 
 /* ------------------------------------------------------------------ */
+/* Shared expert  [moe.rs: a shared gate GEMM gives one logit per token,   */
+/* a shared gate/up GEMM, the gated activation and a shared down GEMM     */
+/* give the shared output, and the token-gated add puts the sigmoid of    */
+/* the token's logit times that output onto the routed output].          */
+/* Here the shared projections have the experts' packed format (one       */
+/* expert, fc1 rows gate/up interleaved) and the shared gate is a dtype   */
+/* vector g[H]:                                                           */
+/*   out[i, h] = sigmoid(sum_h' x[t,h'] g[h']) * fc2_s(act(fc1_s(x_t)))[h] */
+/* with t = tokens[i]; the caller adds it to the routed layer output.     */
+/* ------------------------------------------------------------------ */
+static double sigmoid(double z)
+{
+    return 1.0 / (1.0 + exp(-z));
+}
+
+void oracle_shared_expert(const uint16_t* hidden, int64_t T, int32_t H, int32_t Is,
+                          const uint8_t* fc1_codes, const uint16_t* fc1_scales,
+                          const uint8_t* fc1_zp, int32_t fc1_bits, const uint8_t* fc2_codes,
+                          const uint16_t* fc2_scales, const uint8_t* fc2_zp, int32_t fc2_bits,
+                          double zpo, int32_t block_size, int32_t activation, int32_t dtype,
+                          const uint16_t* gate, const int64_t* tokens, int64_t n_tokens,
+                          double* out)
+{
+    (void)T;
+    const int64_t N1 = 2 * (int64_t)Is;
+    const int64_t widest = H > Is ? H : Is;
+#pragma omp parallel
+    {
+        double* x = (double*)malloc(sizeof(double) * (size_t)H);
+        double* wrow = (double*)malloc(sizeof(double) * (size_t)widest);
+        double* y1 = (double*)malloc(sizeof(double) * (size_t)N1);
+        double* a = (double*)malloc(sizeof(double) * (size_t)Is);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_tokens; ++i) {
+            const int64_t t = tokens[i];
+            double logit = 0.0;
+            for (int32_t h = 0; h < H; ++h) {
+                x[h] = widen(hidden[t * H + h], dtype);
+                logit += x[h] * widen(gate[h], dtype);
+            }
+            const double g = sigmoid(logit);
+            for (int64_t n = 0; n < N1; ++n) {                  /* shared gate/up */
+                dequant_row(fc1_codes, fc1_scales, fc1_zp, n, H, fc1_bits, block_size, zpo, dtype,
+                            NULL, wrow);
+                double acc = 0.0;
+                for (int32_t h = 0; h < H; ++h) {
+                    acc += x[h] * wrow[h];
+                }
+                y1[n] = acc;
+            }
+            for (int32_t j = 0; j < Is; ++j) {
+                a[j] = gated(y1[2 * j], y1[2 * j + 1], activation);
+            }
+            for (int32_t h = 0; h < H; ++h) {                   /* shared down, gated */
+                dequant_row(fc2_codes, fc2_scales, fc2_zp, h, Is, fc2_bits, block_size, zpo, dtype,
+                            NULL, wrow);
+                double acc = 0.0;
+                for (int32_t j = 0; j < Is; ++j) {
+                    acc += a[j] * wrow[j];
+                }
+                out[i * H + h] = g * acc;
+            }
+        }
+        free(x);
+        free(wrow);
+        free(y1);
+        free(a);
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Expert grouping and tile work-list                                   */
 /* [qmoe.rs, launch_grouping: counts, offsets, grouped routes];         */
 /* [gemm_quant_moe.rs, moe_build_tile_worklist: experts ascending]      */

@@ -168,6 +168,23 @@ def make_hidden(T: int, H: int, dtype: int, seed: int) -> np.ndarray:
     return np.ascontiguousarray(_to_dtype_bits(rng.standard_normal((T, H), dtype=np.float32), dtype))
 
 
+def make_shared_expert(spec: dict, I_shared: int, seed: int) -> dict:
+    """One shared expert for ``spec``'s layer, in the experts' packed format
+    (widths, block size, scale range and zero-point mode of ``spec``), plus
+    its gate vector [H] drawn N(0, 1/H) and rounded to the dtype.  Keys:
+    fc1_codes [1, 2*I_shared, H*b/8], fc1_scales, fc1_zp, fc2_codes
+    [1, H, I_shared*b/8], fc2_scales, fc2_zp, gate [H], I."""
+    sub = dict(spec, T=1, I=I_shared, E=1)
+    drawn = make_inputs(sub, seed)
+    rng = np.random.default_rng(seed + 1)
+    H = spec["H"]
+    gate = rng.standard_normal(H, dtype=np.float32) * np.float32(1.0 / math.sqrt(H))
+    out = {k: v for k, v in drawn.items() if k.startswith("fc")}
+    out["gate"] = np.ascontiguousarray(_to_dtype_bits(gate, spec["dtype"]))
+    out["I"] = I_shared
+    return out
+
+
 def seed_for(i: int) -> int:
     """Default seed of named workload ``i``."""
     return 1000 + i

@@ -319,6 +319,45 @@ def test_router_logits_one_hot_rows_pick_hidden_elements():
     assert np.array_equal(oracle.router_logits(np.zeros_like(x), w.view(np.uint16), 1), np.zeros((T, E)))
 
 
+# ---------------------------------------------------------------- shared expert
+@pytest.mark.parametrize("act,dtype,zp_mode", [(0, 1, "sym"), (1, 2, "u8"), (0, 2, "zpo")])
+def test_shared_expert_matches_dense_torch(act, dtype, zp_mode):
+    # sigmoid(x . g) * W2 (act(W1g x) * W1u x) with dense float64 torch ops on
+    # the brute-force dequantized weights
+    spec = synth.custom(T=6, H=64, I=32, E=4, k=2, fc1_bits=4, fc2_bits=2, block_size=16,
+                        dtype=dtype, act=act, zp_mode=zp_mode, zpo=1.5 if zp_mode == "zpo" else math.nan,
+                        zp_range=(0, 3))
+    inp = synth.make_inputs(spec, 8)
+    sh = synth.make_shared_expert(spec, 48, 9)
+    got = oracle.shared_expert(inp, sh, spec)
+    H, Is = spec["H"], 48
+    w1 = bf.dense_weights(sh["fc1_codes"], sh["fc1_scales"], sh["fc1_zp"], H, 4, 16,
+                          spec["zpo"], dtype)[0]
+    w2 = bf.dense_weights(sh["fc2_codes"], sh["fc2_scales"], sh["fc2_zp"], Is, 2, 16,
+                          spec["zpo"], dtype)[0]
+    x = torch.from_numpy(bf.widen(inp["hidden"], dtype))
+    g = torch.sigmoid(x @ torch.from_numpy(bf.widen(sh["gate"], dtype)))
+    y1 = x @ torch.from_numpy(w1).T
+    gate, up = y1[:, 0::2], y1[:, 1::2]
+    a = (F.silu(gate) if act == 0 else F.gelu(gate, approximate="tanh")) * up
+    ref = (g[:, None] * (a @ torch.from_numpy(w2).T)).numpy()
+    assert np.allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_shared_expert_zero_gate_halves_the_ffn():
+    # a zero gate vector: sigmoid(0) = 1/2 exactly, so the contribution is half
+    # the plain shared FFN, which is the layer output with one expert (E = 1,
+    # k = 1 routes every token to it with weight exactly 1)
+    spec = synth.custom(T=5, H=64, I=32, E=1, k=1, fc1_bits=4, fc2_bits=4, block_size=32)
+    inp = synth.make_inputs(spec, 3)
+    sh = {"fc1_codes": inp["fc1_codes"], "fc1_scales": inp["fc1_scales"], "fc1_zp": None,
+          "fc2_codes": inp["fc2_codes"], "fc2_scales": inp["fc2_scales"], "fc2_zp": None,
+          "gate": np.zeros(64, dtype=np.uint16), "I": 32}
+    half = oracle.shared_expert(inp, sh, spec)
+    ref = bf.layer(inp, spec)
+    assert np.allclose(half, 0.5 * ref, rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------------- grouping
 @pytest.mark.parametrize("E,R,m_tile,n_tile,N", [(8, 64, 16, 64, 200), (512, 60, 16, 32, 64),
                                                  (3, 1, 128, 128, 128), (8, 1000, 128, 256, 4096),
