@@ -218,6 +218,36 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The layer with a shared expert [moe.rs: routed experts plus a shared
+ * expert whose output is added to the routed output times the sigmoid of a
+ * per-token gate logit (shared gate GEMM, gated add)].
+ *   fc1, fc2, logits, ... as qmoe_forward (the routed experts)
+ *   I_shared     the shared expert's intermediate size (a multiple of 128
+ *                and of block_size)
+ *   shared_fc1   one expert: N = 2*I_shared interleaved gate/up rows, K = H
+ *   shared_fc2   one expert: N = H rows, K = I_shared
+ *                (same widths rules, block_size and zero_point_offset as the
+ *                routed projections)
+ *   shared_gate  dtype [H] (16-byte aligned): the shared gate's weights
+ *   out          dtype [T, H] out: RNE(routed + s_t * shared_t) with
+ *                s_t = sigmoid(sum_h x[t,h] shared_gate[h]) in float32, the
+ *                routed and shared outputs each rounded to dtype first (as the
+ *                page's weighted sum and shared output are)
+ *   workspace    >= qmoe_shared_workspace_size(...) bytes, 256-byte aligned
+ * Runs qmoe_forward for the routed experts, a token-gate kernel, the shared
+ * expert as a one-expert qmoe_forward, and a gated add.
+ */
+size_t qmoe_shared_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t top_k,
+                                  int32_t I_shared, int32_t dtype);
+int qmoe_forward_shared(const void* hidden, const float* logits, int64_t T, int32_t H, int32_t I,
+                        int32_t E, const qmoe_proj* fc1, const qmoe_proj* fc2, int32_t I_shared,
+                        const qmoe_proj* shared_fc1, const qmoe_proj* shared_fc2,
+                        const void* shared_gate, float zero_point_offset, int32_t block_size,
+                        int32_t top_k, int32_t normalize, int32_t activation, int32_t dtype,
+                        void* out, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
  * qmoe_forward for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
  * same arguments and kernels as qmoe_forward without workspace and

@@ -35,7 +35,8 @@ RAW_SINGLE_BASE = 0
 RAW_MULTI_BASE = 1
 
 EXPORTED = ("qmoe_last_error", "qmoe_route", "qmoe_router", "qmoe_worklist_capacity", "qmoe_group",
-            "qmoe_workspace_size", "qmoe_forward", "qmoe_forward_noalloc", "qmoe_dequantize",
+            "qmoe_workspace_size", "qmoe_forward", "qmoe_forward_noalloc",
+            "qmoe_shared_workspace_size", "qmoe_forward_shared", "qmoe_dequantize",
             "qmoe_raw_codes",
             "qmoe_timer_start", "qmoe_timer_stop")
 
@@ -80,11 +81,18 @@ def load_library(path: str = LIB_PATH):
     lib.qmoe_forward_noalloc.argtypes = [P, P, i64, i32, i32, i32, ctypes.POINTER(_Proj),
                                          ctypes.POINTER(_Proj), f32, i32, i32, i32, i32, i32, P,
                                          P, P, P]
+    lib.qmoe_shared_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32, i32]
+    lib.qmoe_shared_workspace_size.restype = sz
+    lib.qmoe_forward_shared.argtypes = [P, P, i64, i32, i32, i32, ctypes.POINTER(_Proj),
+                                        ctypes.POINTER(_Proj), i32, ctypes.POINTER(_Proj),
+                                        ctypes.POINTER(_Proj), P, f32, i32, i32, i32, i32, i32,
+                                        P, P, P, P, sz, P]
     lib.qmoe_dequantize.argtypes = [ctypes.POINTER(_Proj), i32, i32, i32, i32, f32, i32, P, P, P]
     lib.qmoe_raw_codes.argtypes = [ctypes.POINTER(_Proj), i32, i32, i32, i32, i32, P, P]
     lib.qmoe_timer_start.argtypes = [i32]
     lib.qmoe_timer_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     for name in ("qmoe_route", "qmoe_router", "qmoe_group", "qmoe_forward", "qmoe_forward_noalloc",
+                 "qmoe_forward_shared",
                  "qmoe_dequantize", "qmoe_raw_codes",
                  "qmoe_timer_start", "qmoe_timer_stop"):
         getattr(lib, name).restype = ctypes.c_int
@@ -253,6 +261,50 @@ def forward(hidden: torch.Tensor, logits: torch.Tensor, fc1: Projection, fc2: Pr
         _ptr(hidden), _ptr(logits), T, H, I, E, ctypes.byref(p1), ctypes.byref(p2),
         float(zero_point_offset), block_size, top_k, normalize, activation, dt, _ptr(out),
         _ptr(ids), _ptr(w), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (out, ids, w) if return_routing else out
+
+
+def forward_shared(hidden: torch.Tensor, logits: torch.Tensor, fc1: Projection, fc2: Projection,
+                   shared_fc1: Projection, shared_fc2: Projection, shared_gate: torch.Tensor, *,
+                   top_k: int, block_size: int, normalize: int = 1, activation: int = ACT_SWIGLU,
+                   zero_point_offset: float = math.nan, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, return_routing: bool = False,
+                   stream=None):
+    """The layer with a shared expert: routed output + sigmoid(x . shared_gate) * shared FFN."""
+    dt = dtype_code(hidden.dtype)
+    _dev(hidden, "hidden")
+    T, H = hidden.shape
+    _dev(logits, "logits", torch.float32)
+    E = logits.shape[1]
+    for name, proj in (("fc1", fc1), ("fc2", fc2), ("shared_fc1", shared_fc1),
+                       ("shared_fc2", shared_fc2)):
+        if proj.scales.dtype != hidden.dtype:
+            raise ValueError(f"{name}.scales has dtype {proj.scales.dtype}, expected {hidden.dtype}")
+    I = fc2.codes.shape[2] * 8 // fc2.bits
+    Is = shared_fc2.codes.shape[2] * 8 // shared_fc2.bits
+    p1 = fc1._struct(E, 2 * I, H, block_size, "fc1")
+    p2 = fc2._struct(E, H, I, block_size, "fc2")
+    s1 = shared_fc1._struct(1, 2 * Is, H, block_size, "shared_fc1")
+    s2 = shared_fc2._struct(1, H, Is, block_size, "shared_fc2")
+    _dev(shared_gate, "shared_gate", hidden.dtype, (H,))
+    if out is None:
+        out = torch.empty_like(hidden)
+    _dev(out, "out", hidden.dtype, (T, H))
+    if workspace is None:
+        n = int(load_library().qmoe_shared_workspace_size(T, H, I, E, top_k, Is, dt))
+        if n == 0:
+            raise ValueError("invalid sizes for the shared-expert workspace")
+        workspace = torch.empty(n, dtype=torch.uint8, device=hidden.device)
+    _dev(workspace, "workspace", torch.uint8)
+    ids = w = None
+    if return_routing:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=hidden.device)
+        w = torch.empty((T, top_k), dtype=torch.float32, device=hidden.device)
+    _check(load_library().qmoe_forward_shared(
+        _ptr(hidden), _ptr(logits), T, H, I, E, ctypes.byref(p1), ctypes.byref(p2), Is,
+        ctypes.byref(s1), ctypes.byref(s2), _ptr(shared_gate), float(zero_point_offset),
+        block_size, top_k, normalize, activation, dt, _ptr(out), _ptr(ids), _ptr(w),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
     return (out, ids, w) if return_routing else out
 
 

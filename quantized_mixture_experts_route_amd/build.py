@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["qmoe_api.cpp", "route.hip", "group.hip", "plan.hip", "gemm_prefill.hip", "gemm_decode.hip", "gemm_stream.hip",
-           "combine.hip", "dequant.hip", "noalloc.hip", "router.hip"]
+           "combine.hip", "dequant.hip", "noalloc.hip", "router.hip", "shared.hip"]
 
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          # packed fp32 VALU ops stay off: plain scalar fp32 everywhere

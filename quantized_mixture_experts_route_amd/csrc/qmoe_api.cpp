@@ -570,6 +570,92 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     return ok();
 }
 
+namespace {
+// Workspace of the shared-expert layer: the routed layer's, then the one-expert
+// shared layer's, its dtype output [T, H] and the token gates float32 [T].
+struct SharedLayout {
+    size_t routed, shared, shared_out, gates, total;
+};
+
+bool make_shared_layout(int64_t T, int H, int I, int E, int top_k, int I_shared, int dtype,
+                        SharedLayout* S)
+{
+    const size_t a = qmoe_workspace_size(T, H, I, E, top_k, dtype);
+    const size_t b = qmoe_workspace_size(T, H, I_shared, 1, 1, dtype);
+    int64_t out_bytes;
+    if (a == 0 || b == 0 || !mul_ok(T, (int64_t)H * 2, &out_bytes)) return false;
+    S->routed = 0;
+    S->shared = align_up(a);
+    S->shared_out = S->shared + align_up(b);
+    S->gates = S->shared_out + align_up((size_t)out_bytes);
+    S->total = S->gates + align_up((size_t)T * 4 + 4);
+    return true;
+}
+}  // namespace
+
+size_t qmoe_shared_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t top_k,
+                                  int32_t I_shared, int32_t dtype)
+{
+    SharedLayout S;
+    if (I_shared < 1 || !make_shared_layout(T, H, I, E, top_k, I_shared, dtype, &S)) return 0;
+    return S.total;
+}
+
+int qmoe_forward_shared(const void* hidden, const float* logits, int64_t T, int32_t H, int32_t I,
+                        int32_t E, const qmoe_proj* fc1, const qmoe_proj* fc2, int32_t I_shared,
+                        const qmoe_proj* shared_fc1, const qmoe_proj* shared_fc2,
+                        const void* shared_gate, float zero_point_offset, int32_t block_size,
+                        int32_t top_k, int32_t normalize, int32_t activation, int32_t dtype,
+                        void* out, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                        size_t workspace_bytes, void* stream)
+{
+    int rc;
+    if (I_shared < 1) return fail(QMOE_ERR_INVALID_ARG, "I_shared=%d must be >= 1", I_shared);
+    if ((rc = check_block_size(block_size))) return rc;
+    if (!shared_gate || !aligned(shared_gate, 16)) {
+        return fail(QMOE_ERR_INVALID_ARG, "shared_gate must be non-NULL and 16-byte aligned");
+    }
+    if ((rc = check_proj("shared_fc1", shared_fc1)) || (rc = check_proj("shared_fc2", shared_fc2))) return rc;
+    SharedLayout S;
+    if (!make_shared_layout(T, H, I, E, top_k, I_shared, dtype, &S)) {
+        return fail(QMOE_ERR_INVALID_ARG, "invalid sizes or dtype for the shared-expert layer");
+    }
+    if (I_shared % block_size || I_shared % qmoe::kSuperK) {
+        return fail(QMOE_ERR_UNSUPPORTED, "I_shared=%d must be a multiple of block_size and of %d",
+                    I_shared, qmoe::kSuperK);
+    }
+    if (workspace && workspace_bytes < S.total) {
+        return fail(QMOE_ERR_WORKSPACE, "workspace_bytes=%zu < %zu", workspace_bytes, S.total);
+    }
+    if (!workspace || !aligned(workspace, kAlign)) {
+        return fail(QMOE_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
+    }
+    char* ws = static_cast<char*>(workspace);
+    void* shared_out = ws + S.shared_out;
+    float* gates = reinterpret_cast<float*>(ws + S.gates);
+    hipStream_t s = (hipStream_t)stream;
+    // 1) the routed layer into out (validates every routed argument; T = 0 ends here)
+    if ((rc = qmoe_forward(hidden, logits, T, H, I, E, fc1, fc2, zero_point_offset, block_size, top_k,
+                           normalize, activation, dtype, out, topk_ids_out, topk_w_out,
+                           ws + S.routed, S.shared - S.routed, stream))) {
+        return rc;
+    }
+    if (T == 0) return ok();
+    // 2) token gates s[t] = sigmoid(x_t . g)
+    hipError_t e = qmoe::launch_shared_gate(hidden, shared_gate, T, H, dtype, gates, s);
+    if (e != hipSuccess) return hip_fail(e, "shared gate launch");
+    // 3) the shared expert as a one-expert layer (every token on expert 0 with
+    //    weight exactly 1: the finite gates serve as its one-column logits)
+    if ((rc = qmoe_forward(hidden, gates, T, H, I_shared, 1, shared_fc1, shared_fc2, zero_point_offset,
+                           block_size, 1, 1, activation, dtype, shared_out, nullptr, nullptr,
+                           ws + S.shared, S.shared_out - S.shared, stream))) {
+        return rc;
+    }
+    // 4) out += s[t] * shared_out, rounded once more to dtype
+    e = qmoe::launch_gated_add(out, shared_out, gates, T, H, dtype, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "gated add launch");
+}
+
 int qmoe_dequantize(const qmoe_proj* p, int32_t E, int32_t N, int32_t K, int32_t block_size,
                     float zero_point_offset, int32_t dtype, int32_t* codes_out, void* w_out,
                     void* stream)

@@ -131,6 +131,13 @@ hipError_t launch_router(const void* hidden, const void* gate_weight, int64_t T,
                          int top_k, int normalize, int dtype, float* logits_out, int32_t* ids,
                          float* weights, hipStream_t s);
 
+// Shared expert (shared.hip): s[t] = sigmoid(hidden[t] . gate) in float32,
+// and out[t,h] = RNE(out[t,h] + s[t] * shared[t,h]) in the layer's dtype.
+hipError_t launch_shared_gate(const void* hidden, const void* gate, int64_t T, int H, int dtype,
+                              float* s_out, hipStream_t s);
+hipError_t launch_gated_add(void* out, const void* shared, const float* s_in, int64_t T, int H,
+                            int dtype, hipStream_t s);
+
 hipError_t launch_group(const int32_t* ids, int R, int E, int m_tile, int nt1, int32_t* offsets,
                         int32_t* sorted, int32_t* wl1, int64_t cap1, int32_t* n1, int nt2,
                         int32_t* wl2, int64_t cap2, int32_t* n2, hipStream_t s);

@@ -213,6 +213,26 @@ def test_router_validation():
     assert call(T=0, hidden=None) == qm.OK           # nothing to do
 
 
+def test_shared_validation():
+    lib = qm.load_library()
+    p = _proj()
+    n = lib.qmoe_shared_workspace_size(8, 256, 256, 8, 2, 128, 1)
+    assert n > qm.workspace_size(8, 256, 256, 8, 2, 1)
+    assert lib.qmoe_shared_workspace_size(8, 256, 256, 8, 2, 0, 1) == 0
+
+    def call(I_shared=128, gate=FAKE, bs=32, ws=FAKE, ws_bytes=1 << 30, sp=p):
+        return lib.qmoe_forward_shared(FAKE, FAKE, 8, 256, 256, 8, ctypes.byref(p), ctypes.byref(p),
+                                       I_shared, ctypes.byref(sp), ctypes.byref(sp), gate,
+                                       math.nan, bs, 2, 1, 0, 1, FAKE, None, None, ws, ws_bytes, None)
+
+    assert call(I_shared=0) == qm.ERR_INVALID_ARG
+    assert call(gate=None) == qm.ERR_INVALID_ARG
+    assert call(bs=0) == qm.ERR_INVALID_ARG
+    assert call(I_shared=96) == qm.ERR_UNSUPPORTED       # not a multiple of 128
+    assert call(ws_bytes=n - 1) == qm.ERR_WORKSPACE
+    assert call(sp=_proj(bits=5)) == qm.ERR_INVALID_ARG
+
+
 def test_timer_validation():
     lib = qm.load_library()
     assert lib.qmoe_timer_start(7) == qm.ERR_INVALID_ARG
