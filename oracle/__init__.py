@@ -45,17 +45,30 @@ def _load():
     lib.oracle_widen.argtypes = [P, i64, i32, P]
     lib.oracle_route_key.argtypes = [ctypes.c_float]
     lib.oracle_route_key.restype = i32
-    lib.oracle_route.argtypes = [P, i64, i32, i32, i32, P, P]
+    lib.oracle_route.argtypes = [P, P, i64, i32, i32, i32, P, P]
     lib.oracle_dequant.argtypes = [P, P, P, i64, i32, i32, i32, f64, i32, P, P]
     lib.oracle_forward.argtypes = [P, P, i64, i32, i32, i32,
                                    P, P, P, i32, P, P, P, i32,
-                                   f64, i32, i32, i32, i32, i32, P, i64, P]
+                                   f64, i32, i32, i32, i32, i32, P, i64,
+                                   ctypes.POINTER(_Opts), P]
     lib.oracle_group.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, i64, P]
     lib.oracle_router_logits.argtypes = [P, P, i64, i32, i32, i32, P]
+    lib.oracle_gated.argtypes = [f64, f64, i32, f64, f64, f64]
+    lib.oracle_gated.restype = f64
     lib.oracle_shared_expert.argtypes = [P, i64, i32, i32, P, P, P, i32, P, P, P, i32,
                                          f64, i32, i32, i32, P, P, i64, P]
     _lib = lib
     return lib
+
+
+class _Opts(ctypes.Structure):
+    """Mirror of oracle_opts in qmoe_oracle.c."""
+    _fields_ = [("fc1_bias", ctypes.c_void_p), ("fc2_bias", ctypes.c_void_p),
+                ("fc3_codes", ctypes.c_void_p), ("fc3_scales", ctypes.c_void_p),
+                ("fc3_zp", ctypes.c_void_p), ("fc3_bits", ctypes.c_int32),
+                ("fc3_bias", ctypes.c_void_p), ("router_weights", ctypes.c_void_p),
+                ("swiglu_fusion", ctypes.c_int32), ("alpha", ctypes.c_double),
+                ("beta", ctypes.c_double), ("limit", ctypes.c_double)]
 
 
 def _ptr(a):
@@ -74,6 +87,12 @@ def widen(bits: np.ndarray, dtype: int) -> np.ndarray:
     return out
 
 
+def gated(gate: float, up: float, activation: int, alpha: float = 1.0, beta: float = 0.0,
+          limit: float = float("inf")) -> float:
+    """The gated activation of one (gate, up) pair, with the SwiGLU parameters."""
+    return float(_load().oracle_gated(gate, up, activation, alpha, beta, limit))
+
+
 def route_key(x: float) -> int:
     return int(_load().oracle_route_key(float(np.float32(x))))
 
@@ -90,13 +109,15 @@ def router_logits(hidden: np.ndarray, weight: np.ndarray, dtype: int) -> np.ndar
     return out
 
 
-def route(logits: np.ndarray, top_k: int, normalize: int):
-    """Top-k expert ids (int32 [T, k]) and routing weights (float64 [T, k])."""
+def route(logits: np.ndarray, top_k: int, normalize: int, router_weights=None):
+    """Top-k expert ids (int32 [T, k]) and routing weights (float64 [T, k]); with
+    router_weights (float32 [T, E]) the weights come from it instead of the logits."""
     logits = _c(logits, np.float32)
+    rw = _c(router_weights, np.float32)
     T, E = logits.shape
     ids = np.empty((T, top_k), dtype=np.int32)
     w = np.empty((T, top_k), dtype=np.float64)
-    _load().oracle_route(_ptr(logits), T, E, top_k, normalize, _ptr(ids), _ptr(w))
+    _load().oracle_route(_ptr(logits), _ptr(rw), T, E, top_k, normalize, _ptr(ids), _ptr(w))
     return ids, w
 
 
@@ -142,13 +163,22 @@ def forward(inp: dict, spec: dict, tokens=None) -> np.ndarray:
     arrs = dict(hidden=_c(inp["hidden"], np.uint16), logits=_c(inp["logits"], np.float32),
                 c1=_c(inp["fc1_codes"], np.uint8), s1=_c(inp["fc1_scales"], np.uint16),
                 z1=_c(inp["fc1_zp"], np.uint8), c2=_c(inp["fc2_codes"], np.uint8),
-                s2=_c(inp["fc2_scales"], np.uint16), z2=_c(inp["fc2_zp"], np.uint8))
+                s2=_c(inp["fc2_scales"], np.uint16), z2=_c(inp["fc2_zp"], np.uint8),
+                b1=_c(inp.get("fc1_bias"), np.float32), b2=_c(inp.get("fc2_bias"), np.float32),
+                c3=_c(inp.get("fc3_codes"), np.uint8), s3=_c(inp.get("fc3_scales"), np.uint16),
+                z3=_c(inp.get("fc3_zp"), np.uint8), b3=_c(inp.get("fc3_bias"), np.float32),
+                rw=_c(inp.get("router_weights"), np.float32))
+    opts = _Opts(_ptr(arrs["b1"]), _ptr(arrs["b2"]), _ptr(arrs["c3"]), _ptr(arrs["s3"]),
+                 _ptr(arrs["z3"]), int(spec.get("fc3_bits", spec["fc1_bits"])), _ptr(arrs["b3"]),
+                 _ptr(arrs["rw"]), int(spec.get("swiglu_fusion", 1)),
+                 float(spec.get("alpha", 1.0)), float(spec.get("beta", 0.0)),
+                 float(spec.get("limit", float("inf"))))
     _load().oracle_forward(
         _ptr(arrs["hidden"]), _ptr(arrs["logits"]), T, H, I, E,
         _ptr(arrs["c1"]), _ptr(arrs["s1"]), _ptr(arrs["z1"]), spec["fc1_bits"],
         _ptr(arrs["c2"]), _ptr(arrs["s2"]), _ptr(arrs["z2"]), spec["fc2_bits"],
         float(spec["zpo"]), spec["block_size"], spec["k"], spec["normalize"], spec["act"],
-        spec["dtype"], _ptr(tokens), tokens.size, _ptr(out))
+        spec["dtype"], _ptr(tokens), tokens.size, ctypes.byref(opts), _ptr(out))
     return out
 
 

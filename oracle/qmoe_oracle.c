@@ -116,15 +116,32 @@ static int rank_order(const void* a, const void* b)
  * m is the largest non-NaN logit (NaN entries are skipped, as a running
  * fmax does; -inf if there is none).  Each selected expert's numerator is
  * exp(l - m); the denominator is the sum of the selected numerators when
- * normalize is set, otherwise the sum of exp(l - m) over every expert. */
-static void route_one(const float* logits, int32_t E, int32_t top_k, int32_t normalize,
-                      ranked_expert* scratch, int32_t* ids, double* weights)
+ * normalize is set, otherwise the sum of exp(l - m) over every expert.
+ * With an aggregation row (the operator's router_weights input, [qmoe.rs,
+ * qmoe_route, its router_weights branch]) the logits only select: a
+ * selected expert's weight is its aggregation value, divided by the sum of
+ * the selected values when normalize is set, and 0 when that sum is 0. */
+static void route_one(const float* logits, const float* aggregation, int32_t E, int32_t top_k,
+                      int32_t normalize, ranked_expert* scratch, int32_t* ids, double* weights)
 {
     for (int32_t e = 0; e < E; ++e) {
         scratch[e].key = route_key(logits[e]);
         scratch[e].expert = e;
     }
     qsort(scratch, (size_t)E, sizeof(ranked_expert), rank_order);
+
+    if (aggregation) {
+        double sum = 0.0;
+        for (int32_t s = 0; s < top_k; ++s) {
+            ids[s] = scratch[s].expert;
+            sum += (double)aggregation[ids[s]];
+        }
+        const double denominator = normalize ? sum : 1.0;
+        for (int32_t s = 0; s < top_k; ++s) {
+            weights[s] = denominator == 0.0 ? 0.0 : (double)aggregation[ids[s]] / denominator;
+        }
+        return;
+    }
 
     double m = -INFINITY;
     for (int32_t e = 0; e < E; ++e) {
@@ -151,16 +168,16 @@ static void route_one(const float* logits, int32_t E, int32_t top_k, int32_t nor
     }
 }
 
-void oracle_route(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t normalize,
-                  int32_t* ids, double* weights)
+void oracle_route(const float* logits, const float* router_weights, int64_t T, int32_t E,
+                  int32_t top_k, int32_t normalize, int32_t* ids, double* weights)
 {
 #pragma omp parallel
     {
         ranked_expert* scratch = (ranked_expert*)malloc(sizeof(ranked_expert) * (size_t)E);
 #pragma omp for schedule(static)
         for (int64_t t = 0; t < T; ++t) {
-            route_one(logits + t * E, E, top_k, normalize, scratch, ids + t * top_k,
-                      weights + t * top_k);
+            route_one(logits + t * E, router_weights ? router_weights + t * E : NULL, E, top_k,
+                      normalize, scratch, ids + t * top_k, weights + t * top_k);
         }
         free(scratch);
     }
@@ -270,31 +287,86 @@ void oracle_dequant(const uint8_t* codes, const uint16_t* scales, const uint8_t*
 
 /* ------------------------------------------------------------------ */
 /* Gated activation  [qmoe.rs, qmoe_activate (tanh GELU constants) and  */
-/* swiglu_value with alpha=1, beta=0, no limit]; [PR 32198, GeGLU]      */
+/* swiglu_value; PR 32198, GeGLU]                                       */
+/* SwiGLU: the gate is bounded above by limit (fmin, so a NaN gate      */
+/* becomes limit), the linear part clamped to [-limit, limit] unless it */
+/* is NaN; value = g' * sigmoid(alpha g') * (u' + beta).  The defaults  */
+/* alpha = 1, beta = 0, limit = +inf give silu(g) * u.  GeGLU uses the   */
+/* tanh-GELU gate and takes no parameters.                              */
 /* ------------------------------------------------------------------ */
-static double gated(double gate, double up, int activation)
+typedef struct {
+    double alpha, beta, limit;
+} act_params;
+
+static double gated(double gate, double up, int activation, const act_params* p)
 {
     if (activation == ORACLE_GEGLU) {
         const double inner = 0.7978845608028654 * (gate + 0.044715 * gate * gate * gate);
         return 0.5 * gate * (1.0 + tanh(inner)) * up;
     }
-    return gate / (1.0 + exp(-gate)) * up;
+    const double g = fmin(gate, p->limit);
+    const double u = isnan(up) ? up : fmin(fmax(up, -p->limit), p->limit);
+    return g / (1.0 + exp(-p->alpha * g)) * (u + p->beta);
 }
+
+double oracle_gated(double gate, double up, int32_t activation, double alpha, double beta,
+                    double limit)
+{
+    const act_params p = {alpha, beta, limit};
+    return gated(gate, up, activation, &p);
+}
+
+/* Options of the operator beyond the base layer [qmoe.rs, QMoEKernel and
+ * its attributes]: expert biases added to the float32 projection outputs
+ * (fc1 before the activation), the fc1 gate/up layout (swiglu_fusion 1:
+ * interleaved rows 2j / 2j+1; 2: concatenated halves, gate j and up I + j;
+ * 0: fc1 holds the I gate rows and a separate fc3 projection the I up
+ * rows), the SwiGLU parameters, and router_weights for the routing
+ * weights.  Every pointer may be NULL. */
+typedef struct {
+    const float* fc1_bias;       /* [E, rows of fc1] */
+    const float* fc2_bias;       /* [E, H] */
+    const uint8_t* fc3_codes;
+    const uint16_t* fc3_scales;
+    const uint8_t* fc3_zp;
+    int32_t fc3_bits;
+    const float* fc3_bias;       /* [E, I] */
+    const float* router_weights; /* [T, E] */
+    int32_t swiglu_fusion;
+    double alpha, beta, limit;
+} oracle_opts;
 
 /* ------------------------------------------------------------------ */
 /* The layer, for a subset of tokens.                                   */
 /* out[i, h] = sum_s w[t,s] * fc2_e( act( fc1_e(x_t) ) )[h], t = tokens[i] */
 /* ------------------------------------------------------------------ */
+/* One projection row's dot product with x, plus its bias entry. */
+static double row_dot(const uint8_t* codes, const uint16_t* scales, const uint8_t* zp,
+                      int64_t row, const double* x, int32_t K, int32_t bits, int32_t block_size,
+                      double zpo, int32_t dtype, const float* bias, double* wrow)
+{
+    dequant_row(codes, scales, zp, row, K, bits, block_size, zpo, dtype, NULL, wrow);
+    double acc = 0.0;
+    for (int32_t k = 0; k < K; ++k) {
+        acc += x[k] * wrow[k];
+    }
+    return acc + (bias ? (double)bias[row] : 0.0);
+}
+
 void oracle_forward(const uint16_t* hidden, const float* logits, int64_t T, int32_t H, int32_t I,
                     int32_t E, const uint8_t* fc1_codes, const uint16_t* fc1_scales,
                     const uint8_t* fc1_zp, int32_t fc1_bits, const uint8_t* fc2_codes,
                     const uint16_t* fc2_scales, const uint8_t* fc2_zp, int32_t fc2_bits,
                     double zpo, int32_t block_size, int32_t top_k, int32_t normalize,
                     int32_t activation, int32_t dtype, const int64_t* tokens, int64_t n_tokens,
-                    double* out)
+                    const oracle_opts* opts, double* out)
 {
     (void)T;
-    const int64_t N1 = 2 * (int64_t)I;
+    const oracle_opts none = {NULL, NULL, NULL, NULL, NULL, 0, NULL, NULL, 1, 1.0, 0.0, INFINITY};
+    const oracle_opts* o = opts ? opts : &none;
+    const act_params ap = {o->alpha, o->beta, o->limit};
+    const int fusion = o->swiglu_fusion;
+    const int64_t N1 = fusion == 0 ? (int64_t)I : 2 * (int64_t)I;  /* rows of fc1 per expert */
     const int64_t widest = H > I ? H : I;
 #pragma omp parallel
     {
@@ -303,39 +375,42 @@ void oracle_forward(const uint16_t* hidden, const float* logits, int64_t T, int3
         double* w = (double*)malloc(sizeof(double) * (size_t)top_k);
         double* x = (double*)malloc(sizeof(double) * (size_t)H);
         double* wrow = (double*)malloc(sizeof(double) * (size_t)widest);
-        double* y1 = (double*)malloc(sizeof(double) * (size_t)N1);
         double* a = (double*)malloc(sizeof(double) * (size_t)I);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t i = 0; i < n_tokens; ++i) {
             const int64_t t = tokens[i];
-            double* o = out + i * H;
-            route_one(logits + t * E, E, top_k, normalize, scratch, ids, w);
+            double* out_row = out + i * H;
+            route_one(logits + t * E, o->router_weights ? o->router_weights + t * E : NULL, E,
+                      top_k, normalize, scratch, ids, w);
             for (int32_t h = 0; h < H; ++h) {
                 x[h] = widen(hidden[t * H + h], dtype);
-                o[h] = 0.0;
+                out_row[h] = 0.0;
             }
             for (int32_t s = 0; s < top_k; ++s) {
                 const int64_t e = ids[s];
-                for (int64_t n = 0; n < N1; ++n) {            /* fc1 */
-                    dequant_row(fc1_codes, fc1_scales, fc1_zp, e * N1 + n, H, fc1_bits,
-                                block_size, zpo, dtype, NULL, wrow);
-                    double acc = 0.0;
-                    for (int32_t h = 0; h < H; ++h) {
-                        acc += x[h] * wrow[h];
+                for (int32_t j = 0; j < I; ++j) {             /* fc1 (+ fc3), activation */
+                    int64_t gate_row, up_row;
+                    if (fusion == 1) {
+                        gate_row = 2 * (int64_t)j;
+                        up_row = 2 * (int64_t)j + 1;
+                    } else {
+                        gate_row = j;
+                        up_row = fusion == 2 ? (int64_t)I + j : j;
                     }
-                    y1[n] = acc;
-                }
-                for (int32_t j = 0; j < I; ++j) {             /* gate = 2j, up = 2j+1 */
-                    a[j] = gated(y1[2 * j], y1[2 * j + 1], activation);
+                    const double g = row_dot(fc1_codes, fc1_scales, fc1_zp, e * N1 + gate_row, x, H,
+                                             fc1_bits, block_size, zpo, dtype, o->fc1_bias, wrow);
+                    const double u =
+                        fusion == 0
+                            ? row_dot(o->fc3_codes, o->fc3_scales, o->fc3_zp, e * (int64_t)I + up_row,
+                                      x, H, o->fc3_bits, block_size, zpo, dtype, o->fc3_bias, wrow)
+                            : row_dot(fc1_codes, fc1_scales, fc1_zp, e * N1 + up_row, x, H, fc1_bits,
+                                      block_size, zpo, dtype, o->fc1_bias, wrow);
+                    a[j] = gated(g, u, activation, &ap);
                 }
                 for (int32_t h = 0; h < H; ++h) {             /* fc2, then weighted sum */
-                    dequant_row(fc2_codes, fc2_scales, fc2_zp, e * (int64_t)H + h, I, fc2_bits,
-                                block_size, zpo, dtype, NULL, wrow);
-                    double acc = 0.0;
-                    for (int32_t j = 0; j < I; ++j) {
-                        acc += a[j] * wrow[j];
-                    }
-                    o[h] += w[s] * acc;
+                    const double y = row_dot(fc2_codes, fc2_scales, fc2_zp, e * (int64_t)H + h, a, I,
+                                             fc2_bits, block_size, zpo, dtype, o->fc2_bias, wrow);
+                    out_row[h] += w[s] * y;
                 }
             }
         }
@@ -344,7 +419,6 @@ void oracle_forward(const uint16_t* hidden, const float* logits, int64_t T, int3
         free(w);
         free(x);
         free(wrow);
-        free(y1);
         free(a);
     }
 }
@@ -400,8 +474,9 @@ void oracle_shared_expert(const uint16_t* hidden, int64_t T, int32_t H, int32_t 
                 }
                 y1[n] = acc;
             }
+            const act_params plain = {1.0, 0.0, INFINITY};
             for (int32_t j = 0; j < Is; ++j) {
-                a[j] = gated(y1[2 * j], y1[2 * j + 1], activation);
+                a[j] = gated(y1[2 * j], y1[2 * j + 1], activation, &plain);
             }
             for (int32_t h = 0; h < H; ++h) {                   /* shared down, gated */
                 dequant_row(fc2_codes, fc2_scales, fc2_zp, h, Is, fc2_bits, block_size, zpo, dtype,

@@ -68,12 +68,15 @@ def workload(i: int, **overrides) -> dict:
 
 def custom(T, H, I, E, k, *, fc1_bits=4, fc2_bits=4, block_size=32, dtype=DTYPE_F16,
            act=ACT_SWIGLU, normalize=1, zp_mode="sym", zpo=math.nan, zp_range=None,
-           scale_range=(0.005, 0.02), logit_sigma=1.0, logit_bias=None, name="custom"):
-    """A workload spec for arbitrary (test) shapes."""
-    return dict(name=name, T=T, H=H, I=I, E=E, k=k, normalize=normalize, act=act,
+           scale_range=(0.005, 0.02), logit_sigma=1.0, logit_bias=None, name="custom", **options):
+    """A workload spec for arbitrary (test) shapes.  Options: swiglu_fusion (0, 1, 2),
+    fc3_bits, bias (bool), router_weights (bool), alpha, beta, limit."""
+    spec = dict(name=name, T=T, H=H, I=I, E=E, k=k, normalize=normalize, act=act,
                 dtype=dtype, fc1_bits=fc1_bits, fc2_bits=fc2_bits, block_size=block_size,
                 zp_mode=zp_mode, zpo=zpo, zp_range=zp_range, scale_range=scale_range,
                 logit_sigma=logit_sigma, logit_bias=logit_bias)
+    spec.update(options)
+    return spec
 
 
 def _to_dtype_bits(x32: np.ndarray, dtype: int) -> np.ndarray:
@@ -138,7 +141,9 @@ def make_inputs(spec: dict, seed: int) -> dict:
 
     out = dict(logits=logits, hidden=np.ascontiguousarray(hidden))
     lo_s, hi_s = spec["scale_range"]
-    for name, N, K, bits in (("fc1", 2 * I, H, spec["fc1_bits"]), ("fc2", H, I, spec["fc2_bits"])):
+    fusion = spec.get("swiglu_fusion", 1)
+    n1 = I if fusion == 0 else 2 * I  # fc1 rows: gate only when a separate fc3 holds the up rows
+    for name, N, K, bits in (("fc1", n1, H, spec["fc1_bits"]), ("fc2", H, I, spec["fc2_bits"])):
         row_bytes = K * bits // 8
         codes = rng.integers(0, 256, size=(E, N, row_bytes), dtype=np.uint8)
         n_blocks = K // bs
@@ -151,6 +156,23 @@ def make_inputs(spec: dict, seed: int) -> dict:
         out[name + "_codes"] = codes
         out[name + "_scales"] = np.ascontiguousarray(scales)
         out[name + "_zp"] = zp
+    # operator options, drawn after everything above so the base arrays keep their bytes
+    if fusion == 0:  # the separate up projection fc3 [E, I, H]
+        bits = spec.get("fc3_bits", spec["fc1_bits"])
+        out["fc3_codes"] = rng.integers(0, 256, size=(E, I, H * bits // 8), dtype=np.uint8)
+        s32 = rng.uniform(lo_s, hi_s, size=(E, I, H // bs)).astype(np.float32)
+        out["fc3_scales"] = np.ascontiguousarray(_to_dtype_bits(s32, dtype))
+        out["fc3_zp"] = None
+        if spec.get("zp_mode") == "u8":
+            lo_z, hi_z = spec["zp_range"]
+            out["fc3_zp"] = _draw_zero_points(rng, E, I, H // bs, bits, lo_z, hi_z)
+    if spec.get("bias"):  # float32 expert biases ~ N(0, 0.1^2)
+        out["fc1_bias"] = (rng.standard_normal((E, n1), dtype=np.float32) * np.float32(0.1))
+        out["fc2_bias"] = (rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.1))
+        if fusion == 0:
+            out["fc3_bias"] = (rng.standard_normal((E, I), dtype=np.float32) * np.float32(0.1))
+    if spec.get("router_weights"):  # aggregation weights, uniform in [0, 1)
+        out["router_weights"] = rng.random((T, E), dtype=np.float32)
     return out
 
 

@@ -97,25 +97,47 @@ def gate_activation(g: np.ndarray, act: int) -> np.ndarray:
 
 
 def layer(inp: dict, spec: dict) -> np.ndarray:
-    """Whole-layer output [T, H] in float64: all experts computed densely, then mixed."""
+    """Whole-layer output [T, H] in float64: all experts computed densely, then mixed.
+
+    Options (default SwiGLU/GeGLU parameters only): expert biases, the three
+    gate/up layouts (swiglu_fusion 1 interleaved, 2 halves, 0 a separate fc3),
+    and router_weights as the weights of the selected experts."""
     T, H, I, E, k = spec["T"], spec["H"], spec["I"], spec["E"], spec["k"]
     dt = spec["dtype"]
+    fusion = spec.get("swiglu_fusion", 1)
     x = widen(inp["hidden"], dt)
     w1 = dense_weights(inp["fc1_codes"], inp["fc1_scales"], inp["fc1_zp"], H, spec["fc1_bits"],
                        spec["block_size"], spec["zpo"], dt)
     w2 = dense_weights(inp["fc2_codes"], inp["fc2_scales"], inp["fc2_zp"], I, spec["fc2_bits"],
                        spec["block_size"], spec["zpo"], dt)
+    if fusion == 0:
+        w3 = dense_weights(inp["fc3_codes"], inp["fc3_scales"], inp["fc3_zp"], H,
+                           spec.get("fc3_bits", spec["fc1_bits"]), spec["block_size"], spec["zpo"], dt)
     ids = route(inp["logits"], k)
-    wts = route_weights(inp["logits"], ids, spec["normalize"])
+    rw = inp.get("router_weights")
+    if rw is None:
+        wts = route_weights(inp["logits"], ids, spec["normalize"])
+    else:
+        picked = np.take_along_axis(rw.astype(np.float64), ids.astype(np.int64), 1)
+        den = picked.sum(axis=1, keepdims=True) if spec["normalize"] else np.ones((T, 1))
+        wts = np.where(den == 0, 0.0, picked / np.where(den == 0, 1.0, den))
     mix = np.zeros((T, E))
     for t in range(T):
         for s in range(k):
             mix[t, ids[t, s]] += wts[t, s]
+    b1, b2, b3 = inp.get("fc1_bias"), inp.get("fc2_bias"), inp.get("fc3_bias")
     out = np.zeros((T, H))
     for e in range(E):
-        y1 = x @ w1[e].T
-        a = gate_activation(y1[:, 0::2], spec["act"]) * y1[:, 1::2]
-        out += mix[:, e:e + 1] * (a @ w2[e].T)
+        y1 = x @ w1[e].T + (0.0 if b1 is None else b1[e].astype(np.float64))
+        if fusion == 1:
+            g, u = y1[:, 0::2], y1[:, 1::2]
+        elif fusion == 2:
+            g, u = y1[:, :I], y1[:, I:]
+        else:
+            g, u = y1, x @ w3[e].T + (0.0 if b3 is None else b3[e].astype(np.float64))
+        a = gate_activation(g, spec["act"]) * u
+        y2 = a @ w2[e].T + (0.0 if b2 is None else b2[e].astype(np.float64))
+        out += mix[:, e:e + 1] * y2
     return out
 
 

@@ -71,7 +71,7 @@ def test_bf16_widening_matches_torch_for_every_pattern():
 
 
 # ---------------------------------------------------------------- unpacking
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 def test_unpack_matches_little_endian_bitstream(bits):
     rng = np.random.default_rng(7 + bits)
     K = 256
@@ -81,7 +81,7 @@ def test_unpack_matches_little_endian_bitstream(bits):
     assert np.array_equal(q, bf.unpack_bitstream(codes, bits, K))
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 def test_pack_unpack_round_trip(bits):
     rng = np.random.default_rng(11 + bits)
     K = 128
@@ -130,7 +130,7 @@ def test_symmetric_centres():
         assert np.all(w[0, 8:] == -centre * 0.5)
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 def test_uint8_zero_points_take_precedence_over_offset(bits):
     rng = np.random.default_rng(3)
     K, bs = 64, 16
@@ -149,7 +149,7 @@ def test_uint8_zero_points_take_precedence_over_offset(bits):
 
 def test_dequant_matches_dense_bruteforce_all_modes():
     rng = np.random.default_rng(5)
-    for bits in (2, 3, 4):
+    for bits in (1, 2, 3, 4, 8):
         for dtype in (1, 2):
             for mode in ("sym", "zpo", "u8"):
                 K, bs, N = 128, 32, 6
@@ -165,6 +165,85 @@ def test_dequant_matches_dense_bruteforce_all_modes():
                 _, w = oracle.dequant(codes, scales, zp, K, bits, bs, zpo, dtype)
                 ref = bf.dense_weights(codes, scales, zp, K, bits, bs, zpo, dtype)
                 assert np.array_equal(w, ref), (bits, dtype, mode)
+
+
+# ---------------------------------------------------------------- activation parameters
+def test_swiglu_defaults_are_silu_and_geglu_ignores_parameters():
+    g = np.linspace(-9.0, 9.0, 37)
+    u = np.linspace(2.0, -3.0, 37)
+    silu = F.silu(torch.from_numpy(g)).numpy() * u
+    gelu = F.gelu(torch.from_numpy(g), approximate="tanh").numpy() * u
+    for i in range(g.size):
+        assert math.isclose(oracle.gated(g[i], u[i], 0), silu[i], rel_tol=1e-14, abs_tol=1e-300)
+        v = oracle.gated(g[i], u[i], 1, alpha=3.0, beta=0.5, limit=0.25)
+        assert math.isclose(v, gelu[i], rel_tol=1e-14, abs_tol=1e-300)
+
+
+def test_swiglu_alpha_beta_limit_properties():
+    # [qmoe.rs, swiglu_value]: gate bounded above by the limit, linear part
+    # clamped to [-limit, limit], value = g' * sigmoid(alpha g') * (u' + beta)
+    L = 1.5
+    for g in (-4.0, -0.5, 0.0, 0.7, 1.2):
+        for u in (-1.0, 0.3, 1.4):
+            # alpha = 2: g * sigmoid(2g) = silu(2g) / 2 (textbook routine), inside the limit
+            want = F.silu(torch.tensor(2.0 * g, dtype=torch.float64)).item() / 2.0 * u
+            assert math.isclose(oracle.gated(g, u, 0, alpha=2.0, limit=L), want, rel_tol=1e-14,
+                                abs_tol=1e-300)
+            # beta enters linearly: f(beta) - f(0) = beta * f(u = 1)
+            d = oracle.gated(g, u, 0, beta=0.75, limit=L) - oracle.gated(g, u, 0, limit=L)
+            assert math.isclose(d, 0.75 * oracle.gated(g, 1.0, 0, limit=L), rel_tol=1e-12,
+                                abs_tol=1e-15)
+    # above the limit the gate no longer matters; the linear part saturates at +-limit
+    assert oracle.gated(7.0, 0.5, 0, limit=L) == oracle.gated(L, 0.5, 0, limit=L)
+    assert oracle.gated(0.8, 9.0, 0, limit=L) == oracle.gated(0.8, L, 0, limit=L)
+    assert oracle.gated(0.8, -9.0, 0, limit=L) == oracle.gated(0.8, -L, 0, limit=L)
+    # a NaN linear part stays NaN; a NaN gate is bounded to the limit (fmin)
+    assert math.isnan(oracle.gated(0.8, float("nan"), 0, limit=L))
+    assert oracle.gated(float("nan"), 0.5, 0, limit=L) == oracle.gated(L, 0.5, 0, limit=L)
+
+
+# ---------------------------------------------------------------- operator options
+OPTION_CASES = [
+    dict(bias=True),
+    dict(swiglu_fusion=2),
+    dict(swiglu_fusion=0),
+    dict(swiglu_fusion=0, bias=True, fc3_bits=2),
+    dict(router_weights=True),
+    dict(router_weights=True, normalize=0),
+    dict(fc1_bits=8, fc2_bits=1),
+    dict(fc1_bits=1, fc2_bits=8, zp_mode="u8", zp_range=(0, 1)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(OPTION_CASES)))
+def test_layer_options_match_dense_bruteforce(case):
+    opts = dict(OPTION_CASES[case])
+    spec = synth.custom(T=9, H=64, I=32, E=5, k=2, block_size=16, act=case % 2,
+                        dtype=1 + case % 2, **opts)
+    if spec.get("zp_mode") == "u8" and spec.get("zp_range") is None:
+        spec["zp_range"] = (0, 3)
+    inp = synth.make_inputs(spec, 70 + case)
+    got = oracle.forward(inp, spec)
+    ref = bf.layer(inp, spec)
+    assert np.allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_router_weights_select_by_logits_and_weigh_by_aggregation():
+    rng = np.random.default_rng(12)
+    logits = rng.standard_normal((30, 16)).astype(np.float32)
+    rw = rng.random((30, 16), dtype=np.float32)
+    rw[3, :] = 0.0  # all-zero aggregation: weights 0
+    ids0, _ = oracle.route(logits, 4, 1)
+    ids, w = oracle.route(logits, 4, 0, router_weights=rw)
+    assert np.array_equal(ids, ids0)  # selection by the logits alone
+    assert np.array_equal(w, np.take_along_axis(rw, ids.astype(np.int64), 1).astype(np.float64))
+    ids, w = oracle.route(logits, 4, 1, router_weights=rw)
+    assert np.array_equal(ids, ids0)
+    ok = np.arange(30) != 3
+    assert np.allclose(w[ok].sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    picked = np.take_along_axis(rw, ids.astype(np.int64), 1).astype(np.float64)
+    assert np.allclose(w[ok] * picked[ok][:, :1], picked[ok] * w[ok][:, :1], rtol=1e-14, atol=0)
+    assert np.all(w[3] == 0.0)
 
 
 # ---------------------------------------------------------------- routing
