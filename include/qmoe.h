@@ -80,7 +80,9 @@ extern "C" {
  *   zero_points  NULL, or uint8 [E, N, Z]: bits-wide values packed like the
  *                2/4-bit codes with Z = ceil((K/block_size)/(8/bits)), or one
  *                byte per block for bits = 3 (Z = K/block_size).
- *   bits         2, 3 or 4.
+ *   bits         1, 2, 3, 4 or 8 (1 and 8 as [qmoe.rs, QMoEFactory::create]
+ *                accepts them: codes packed LSB-first like 2/4 bits, centre
+ *                2^(bits-1)).
  * Dequantized weight: W[e,n,kk] = (code - zp) * scale[e,n,kk/block_size]
  * where zp is the zero_points entry if the tensor is given, else the layer's
  * zero_point_offset if it is not NaN, else the symmetric centre 2^(bits-1)
@@ -189,7 +191,7 @@ size_t qmoe_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t t
  *   workspace   >= qmoe_workspace_size(T, H, I, E, top_k, dtype) bytes,
  *               256-byte aligned; contents on entry do not matter.
  * Requires 1 <= E <= 1024, 1 <= top_k <= E, H and I multiples of 128,
- * bits in {2,3,4} per projection, T*H < 2^32 and T*top_k*I < 2^32 (the
+ * bits in {1,2,3,4,8} per projection, T*H < 2^32 and T*top_k*I < 2^32 (the
  * projection kernels address their inputs with 32-bit element offsets).
  * T = 0 returns QMOE_OK and enqueues nothing.
  * Launches: prefill (T*top_k > QMOE_DECODE_MAX_ROUTES) route, group, fc1,
@@ -269,6 +271,58 @@ int qmoe_forward_noalloc(const void* hidden, const float* logits, int64_t T, int
                          int32_t* topk_ids_out, float* topk_w_out, void* stream);
 
 /*
+ * Operator options beyond the base layer [qmoe.rs, the QMoE operator's
+ * optional inputs and attributes].  Zero-initialising the struct is NOT the
+ * default: use QMOE_LAYER_OPTS_DEFAULT, or pass NULL to qmoe_forward_ex.
+ *   fc1_bias       NULL or float32 [E, rows of fc1] (2*I, or I with a separate
+ *                  fc3), added to fc1's float32 outputs before the activation
+ *   fc2_bias       NULL or float32 [E, H], added to fc2's outputs
+ *   fc3            NULL, or (swiglu_fusion = 0) the up projection [E, I, H]:
+ *                  fc1 then holds the I gate rows; fc3 must have fc1's width
+ *                  and zero-point mode (else QMOE_ERR_UNSUPPORTED)
+ *   fc3_bias       NULL or float32 [E, I] (only with fc3)
+ *   router_weights NULL or float32 [T, E]: the logits only select the
+ *                  experts; a selected expert's weight is its router_weights
+ *                  value, divided by the slot-order sum of the selected values
+ *                  when normalize is set (0 when that sum is 0)
+ *   swiglu_fusion  QMOE_SWIGLU_INTERLEAVED (fc1 rows 2j gate, 2j+1 up),
+ *                  QMOE_SWIGLU_HALVES (gate j, up I + j) or
+ *                  QMOE_SWIGLU_SEPARATE (gate in fc1, up in fc3); the last two
+ *                  only with QMOE_ACT_SWIGLU [qmoe.rs, swiglu_fusion 1 / 2 / 0]
+ *   activation_alpha, activation_beta, swiglu_limit   SwiGLU as
+ *                  g' sigmoid(alpha g') (u' + beta), g' = fminf(g, limit),
+ *                  u' = u clamped to [-limit, limit] (NaN stays NaN)
+ *                  [qmoe.rs, swiglu_value]; GeGLU ignores them
+ * Layers with biases, a non-interleaved layout, router_weights or 1/8-bit
+ * codes run on the generic kernels (prefill tiles; decode plan + m-tile
+ * kernels).
+ */
+#define QMOE_SWIGLU_SEPARATE 0
+#define QMOE_SWIGLU_INTERLEAVED 1
+#define QMOE_SWIGLU_HALVES 2
+typedef struct qmoe_layer_opts {
+    const float* fc1_bias;
+    const float* fc2_bias;
+    const qmoe_proj* fc3;
+    const float* fc3_bias;
+    const float* router_weights;
+    int32_t swiglu_fusion;
+    float activation_alpha;
+    float activation_beta;
+    float swiglu_limit;
+} qmoe_layer_opts;
+#define QMOE_LAYER_OPTS_DEFAULT \
+    {NULL, NULL, NULL, NULL, NULL, QMOE_SWIGLU_INTERLEAVED, 1.0f, 0.0f, __builtin_inff()}
+
+/* qmoe_forward with operator options (opts NULL = qmoe_forward). */
+int qmoe_forward_ex(const void* hidden, const float* logits, int64_t T, int32_t H, int32_t I,
+                    int32_t E, const qmoe_proj* fc1, const qmoe_proj* fc2, float zero_point_offset,
+                    int32_t block_size, int32_t top_k, int32_t normalize, int32_t activation,
+                    int32_t dtype, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                    const qmoe_layer_opts* opts, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
  * Test hook: the dequantization of the weight-rounding kernels, written out
  * in full [qmoe.rs, decode_affine_weight: (code - zp) * scale with the code
  * read LSB-first and the zero point from the tensor or the centre; PR 32198,
@@ -301,7 +355,8 @@ int qmoe_dequantize(const qmoe_proj* p, int32_t E, int32_t N, int32_t K, int32_t
  *               the streamed decode kernels, 2/4 bits
  *   codes_out   int32 [E, N, K] out
  * Requires K a multiple of 32.  Errors as qmoe_dequantize; 3-bit codes with
- * QMOE_RAW_MULTI_BASE return QMOE_ERR_UNSUPPORTED.
+ * QMOE_RAW_MULTI_BASE, and 1- and 8-bit codes (no kernel feeds them raw),
+ * return QMOE_ERR_UNSUPPORTED.
  */
 #define QMOE_RAW_SINGLE_BASE 0
 #define QMOE_RAW_MULTI_BASE 1

@@ -35,7 +35,7 @@ RAW_SINGLE_BASE = 0
 RAW_MULTI_BASE = 1
 
 EXPORTED = ("qmoe_last_error", "qmoe_route", "qmoe_router", "qmoe_worklist_capacity", "qmoe_group",
-            "qmoe_workspace_size", "qmoe_forward", "qmoe_forward_noalloc",
+            "qmoe_workspace_size", "qmoe_forward", "qmoe_forward_ex", "qmoe_forward_noalloc",
             "qmoe_shared_workspace_size", "qmoe_forward_shared", "qmoe_dequantize",
             "qmoe_raw_codes",
             "qmoe_timer_start", "qmoe_timer_stop")
@@ -50,6 +50,17 @@ class QMoEError(RuntimeError):
 class _Proj(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("zero_points", ctypes.c_void_p), ("bits", ctypes.c_int32)]
+
+
+class _LayerOpts(ctypes.Structure):
+    _fields_ = [("fc1_bias", ctypes.c_void_p), ("fc2_bias", ctypes.c_void_p),
+                ("fc3", ctypes.POINTER(_Proj)), ("fc3_bias", ctypes.c_void_p),
+                ("router_weights", ctypes.c_void_p), ("swiglu_fusion", ctypes.c_int32),
+                ("activation_alpha", ctypes.c_float), ("activation_beta", ctypes.c_float),
+                ("swiglu_limit", ctypes.c_float)]
+
+
+SWIGLU_SEPARATE, SWIGLU_INTERLEAVED, SWIGLU_HALVES = 0, 1, 2
 
 
 _lib = None
@@ -78,6 +89,9 @@ def load_library(path: str = LIB_PATH):
     lib.qmoe_forward.argtypes = [P, P, i64, i32, i32, i32, ctypes.POINTER(_Proj),
                                  ctypes.POINTER(_Proj), f32, i32, i32, i32, i32, i32, P, P, P, P,
                                  sz, P]
+    lib.qmoe_forward_ex.argtypes = [P, P, i64, i32, i32, i32, ctypes.POINTER(_Proj),
+                                    ctypes.POINTER(_Proj), f32, i32, i32, i32, i32, i32, P, P, P,
+                                    ctypes.POINTER(_LayerOpts), P, sz, P]
     lib.qmoe_forward_noalloc.argtypes = [P, P, i64, i32, i32, i32, ctypes.POINTER(_Proj),
                                          ctypes.POINTER(_Proj), f32, i32, i32, i32, i32, i32, P,
                                          P, P, P]
@@ -91,7 +105,8 @@ def load_library(path: str = LIB_PATH):
     lib.qmoe_raw_codes.argtypes = [ctypes.POINTER(_Proj), i32, i32, i32, i32, i32, P, P]
     lib.qmoe_timer_start.argtypes = [i32]
     lib.qmoe_timer_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
-    for name in ("qmoe_route", "qmoe_router", "qmoe_group", "qmoe_forward", "qmoe_forward_noalloc",
+    for name in ("qmoe_route", "qmoe_router", "qmoe_group", "qmoe_forward", "qmoe_forward_ex",
+                 "qmoe_forward_noalloc",
                  "qmoe_forward_shared",
                  "qmoe_dequantize", "qmoe_raw_codes",
                  "qmoe_timer_start", "qmoe_timer_stop"):
@@ -231,8 +246,19 @@ def forward(hidden: torch.Tensor, logits: torch.Tensor, fc1: Projection, fc2: Pr
             top_k: int, block_size: int, normalize: int = 1, activation: int = ACT_SWIGLU,
             zero_point_offset: float = math.nan, out: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None, return_routing: bool = False,
-            stream=None):
-    """The QMoE layer: out [T, H] in hidden's dtype (plus routing if asked)."""
+            stream=None, fc1_bias: Optional[torch.Tensor] = None,
+            fc2_bias: Optional[torch.Tensor] = None, fc3: Optional[Projection] = None,
+            fc3_bias: Optional[torch.Tensor] = None,
+            router_weights: Optional[torch.Tensor] = None,
+            swiglu_fusion: int = SWIGLU_INTERLEAVED, activation_alpha: float = 1.0,
+            activation_beta: float = 0.0, swiglu_limit: float = math.inf):
+    """The QMoE layer: out [T, H] in hidden's dtype (plus routing if asked).
+
+    The keyword options after ``stream`` are the operator's optional inputs and
+    attributes (qmoe_forward_ex): expert biases (float32), a separate up
+    projection fc3 with swiglu_fusion = SWIGLU_SEPARATE, the gate/up halves
+    layout SWIGLU_HALVES, router_weights (float32 [T, E]) and the SwiGLU
+    parameters."""
     dt = dtype_code(hidden.dtype)
     _dev(hidden, "hidden")
     T, H = hidden.shape
@@ -245,7 +271,8 @@ def forward(hidden: torch.Tensor, logits: torch.Tensor, fc1: Projection, fc2: Pr
         if proj.scales.dtype != hidden.dtype:
             raise ValueError(f"{name}.scales has dtype {proj.scales.dtype}, expected {hidden.dtype}")
     I = fc2.codes.shape[2] * 8 // fc2.bits
-    p1 = fc1._struct(E, 2 * I, H, block_size, "fc1")
+    n1 = I if swiglu_fusion == SWIGLU_SEPARATE else 2 * I
+    p1 = fc1._struct(E, n1, H, block_size, "fc1")
     p2 = fc2._struct(E, H, I, block_size, "fc2")
     if out is None:
         out = torch.empty_like(hidden)
@@ -257,10 +284,23 @@ def forward(hidden: torch.Tensor, logits: torch.Tensor, fc1: Projection, fc2: Pr
     if return_routing:
         ids = torch.empty((T, top_k), dtype=torch.int32, device=hidden.device)
         w = torch.empty((T, top_k), dtype=torch.float32, device=hidden.device)
-    _check(load_library().qmoe_forward(
+    p3 = None
+    if fc3 is not None:
+        if fc3.scales.dtype != hidden.dtype:
+            raise ValueError(f"fc3.scales has dtype {fc3.scales.dtype}, expected {hidden.dtype}")
+        p3 = fc3._struct(E, I, H, block_size, "fc3")
+    for name, b, shape in (("fc1_bias", fc1_bias, (E, n1)), ("fc2_bias", fc2_bias, (E, H)),
+                           ("fc3_bias", fc3_bias, (E, I)), ("router_weights", router_weights, (T, E))):
+        if b is not None:
+            _dev(b, name, torch.float32, shape)
+    opts = _LayerOpts(_ptr(fc1_bias), _ptr(fc2_bias), ctypes.pointer(p3) if p3 is not None else None,
+                      _ptr(fc3_bias), _ptr(router_weights), int(swiglu_fusion),
+                      float(activation_alpha), float(activation_beta), float(swiglu_limit))
+    _check(load_library().qmoe_forward_ex(
         _ptr(hidden), _ptr(logits), T, H, I, E, ctypes.byref(p1), ctypes.byref(p2),
         float(zero_point_offset), block_size, top_k, normalize, activation, dt, _ptr(out),
-        _ptr(ids), _ptr(w), _ptr(workspace), workspace.numel(), _stream(stream)))
+        _ptr(ids), _ptr(w), ctypes.byref(opts), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
     return (out, ids, w) if return_routing else out
 
 

@@ -104,9 +104,11 @@ hipError_t launch_dt(const ProjArgs& w, int64_t rows, int K, int block_size, int
                      uint16_t* w_out, hipStream_t s)
 {
     switch (w.bits) {
+    case 1: return launch_zp<DT, 1>(w, rows, K, block_size, codes_out, w_out, s);
     case 2: return launch_zp<DT, 2>(w, rows, K, block_size, codes_out, w_out, s);
     case 3: return launch_zp<DT, 3>(w, rows, K, block_size, codes_out, w_out, s);
     case 4: return launch_zp<DT, 4>(w, rows, K, block_size, codes_out, w_out, s);
+    case 8: return launch_zp<DT, 8>(w, rows, K, block_size, codes_out, w_out, s);
     default: return hipErrorInvalidValue;
     }
 }

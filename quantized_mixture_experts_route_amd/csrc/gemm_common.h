@@ -25,7 +25,7 @@ struct WeightRow {
     int bits;
 
     // byte of the zero-point row holding block blk's value
-    __device__ uint32_t zp_byte(int blk) const { return zp[bits == 3 ? blk : blk >> (bits == 2 ? 2 : 1)]; }
+    __device__ uint32_t zp_byte(int blk) const { return zp[bits == 3 ? blk : blk / (8 / bits)]; }
 };
 
 __device__ inline WeightRow weight_row(const ProjArgs& w, int64_t row, int K, int block_size)
@@ -110,10 +110,29 @@ __device__ inline void load_a_span(const uint16_t* row, int k, uint32_t (&v)[16]
     }
 }
 
+// SwiGLU with the operator's parameters [qmoe.rs, swiglu_value]: the gate
+// bounded above by limit (fminf), the linear part clamped to [-limit, limit]
+// unless NaN, then g * sigmoid(alpha g) * (u + beta).  alpha = 1, beta = 0,
+// limit = +inf give silu(g) * u.  GeGLU takes no parameters.
 template <int DT>
-__device__ inline float act_value(int act, float gate, float up)
+__device__ inline float act_value(int act, float gate, float up, const ActParams& ap)
 {
-    return act == kGeGLU ? gated<kGeGLU>(gate, up) : gated<kSwiGLU>(gate, up);
+    if (act == kGeGLU) return gated<kGeGLU>(gate, up);
+    const float g = fminf(gate, ap.limit);
+    const float u = isnan(up) ? up : fminf(fmaxf(up, -ap.limit), ap.limit);
+    const float z = ap.alpha * g;
+    const float e = expf(-fabsf(z));
+    const float sig = z >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
+    return g * sig * (u + ap.beta);
+}
+
+// fc1 (+ fc3) weight row of a gate or up row of activation column j, by the
+// gate/up layout [qmoe.rs, swiglu_fusion]: 1 interleaved (gate 2j, up 2j+1),
+// 2 halves (gate j, up I + j), 0 a separate fc3 (gate j of fc1, up j of fc3).
+__device__ inline int64_t fc1_row(int fusion, int j, bool up, int I)
+{
+    if (fusion == 1) return 2 * (int64_t)j + (up ? 1 : 0);
+    return (int64_t)j + (fusion == 2 && up ? I : 0);
 }
 
 // fc2 row values of a decode launch that folds the combine in are written

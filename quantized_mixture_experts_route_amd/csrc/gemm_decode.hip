@@ -68,7 +68,19 @@ __device__ inline int64_t block_rows(const ProjLaunch& p, int e, int n, int c, i
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         trow[nb] = FC1 ? 32 * (nb / 2) + 2 * c + (nb & 1) : 16 * nb + c;
-        wr[nb] = weight_row(p.w, wrow0 + trow[nb], p.K, p.block_size);
+        if (FC1 && p.fusion != 1) {
+            // gate/up halves or a separate fc3: block nb is the gate (even) or up
+            // (odd) row of activation column col0 + 16 (nb / 2) + c
+            const int I = p.N / 2;
+            const bool up = nb & 1;
+            const bool sep = p.fusion == 0;
+            const int64_t rows_e = sep ? I : p.N;
+            wr[nb] = weight_row(sep && up ? p.w3 : p.w,
+                                (int64_t)e * rows_e + fc1_row(p.fusion, col0 + 16 * (nb / 2) + c, up, I),
+                                p.K, p.block_size);
+        } else {
+            wr[nb] = weight_row(p.w, wrow0 + trow[nb], p.K, p.block_size);
+        }
     }
     return wrow0;
 }
@@ -214,7 +226,7 @@ __device__ inline void mfma_chunk(f32x4 (&acc)[NB], const ChunkLoads<BITS, NB>& 
 // float32 values at y2 row out_row(m).  Starts and ends with a barrier.
 template <int DT, bool FC1, int NB, int MTR, class OutRow>
 __device__ inline void reduce_store(uint32_t* lds, const f32x4 (&acc)[NB], const ProjLaunch& p,
-                                    int rows, int col0, int tid, int wave, int g, int c,
+                                    int e, int rows, int col0, int tid, int wave, int g, int c,
                                     OutRow out_row)
 {
     constexpr int kCols = NB * 16;
@@ -242,8 +254,16 @@ __device__ inline void reduce_store(uint32_t* lds, const f32x4 (&acc)[NB], const
                 gate += red[(w * MTR + m) * (kCols + 1) + gate_col];
                 up += red[(w * MTR + m) * (kCols + 1) + gate_col + 16];
             }
+            if (p.bias || p.bias3) {  // expert biases of the gate and up rows
+                const bool sep = p.fusion == 0;
+                const int64_t base = (int64_t)e * (sep ? I : p.N);
+                if (p.bias) gate += p.bias[base + fc1_row(p.fusion, col0 + j, false, I)];
+                if (sep ? p.bias3 != nullptr : p.bias != nullptr) {
+                    up += sep ? p.bias3[base + col0 + j] : p.bias[base + fc1_row(p.fusion, col0 + j, true, I)];
+                }
+            }
             uint16_t* out = reinterpret_cast<uint16_t*>(p.act_out) + (int64_t)out_row(m) * I;
-            out[col0 + j] = Dt<DT>::from_float(act_value<DT>(p.act, gate, up));
+            out[col0 + j] = Dt<DT>::from_float(act_value<DT>(p.act, gate, up, p.ap));
         }
     } else {
         for (int o = tid; o < MTR * kCols; o += kThreads) {
@@ -253,6 +273,7 @@ __device__ inline void reduce_store(uint32_t* lds, const f32x4 (&acc)[NB], const
             float v = 0.f;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) v += red[(w * MTR + m) * (kCols + 1) + h];
+            if (p.bias) v += p.bias[(int64_t)e * p.N + col0 + h];
             store_y2(&p.y2[(int64_t)out_row(m) * p.N + col0 + h], v, p.fused.counters != nullptr);
         }
     }
@@ -336,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(ProjLaunch p,
 
         // 5) partial tiles summed, then the epilogue (fc1: sorted position row0 + m;
         //    fc2: the row's route id)
-        reduce_store<DT, FC1, NB, kDecodeMT>(lds, acc, p, rows, col0, tid, wave, g, c, [&](int m) {
+        reduce_store<DT, FC1, NB, kDecodeMT>(lds, acc, p, e, rows, col0, tid, wave, g, c, [&](int m) {
             return FC1 ? row0 + m : it[kDecodeTileRoutes + m];
         });
         if constexpr (!FC1) {  // one arrival per m-tile on column block n
@@ -488,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_rows_kernel(ProjLaunch p,
             if (m < rows && c < 8) {
                 const int I = p.N / 2;
                 uint16_t* out = reinterpret_cast<uint16_t*>(p.act_out) + (int64_t)(row0 + m) * I;
-                out[n * (kRowsItem / 2) + 8 * wave + c] = Dt<DT>::from_float(act_value<DT>(p.act, sum[i], up));
+                out[n * (kRowsItem / 2) + 8 * wave + c] = Dt<DT>::from_float(act_value<DT>(p.act, sum[i], up, p.ap));
             }
         } else {
             if (m < rows) {
@@ -696,7 +717,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_expert_kernel(ProjLaunch p
         for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         mfma_chunk<DT, BITS, NB, ZP, RAW, STAGED>(acc, L, lds, sc_tab, trow, wr, p, 0, n_super,
                                                   rows, wave, g, c, magic);
-        reduce_store<DT, FC1, NB, kExpertRows>(lds, acc, p, rows, col0, tid, wave, g, c, [&](int m) {
+        reduce_store<DT, FC1, NB, kExpertRows>(lds, acc, p, e, rows, col0, tid, wave, g, c, [&](int m) {
             return FC1 ? first + m0 + m : q.sorted[first + m0 + m];
         });
     }
@@ -731,11 +752,16 @@ template <bool FC1, int DT, int NB, int BITS>
 hipError_t launch_zp(const ProjLaunch& p, const DecodePlan* plan, hipStream_t s)
 {
     const int zp = zp_mode(p.w);
-    const bool staged = zp != kZpTensor && can_stage(p);
-    if (p.block_size % kSuperK == 0) {  // zero point applied in float32: any value works
-        if (zp == kZpTensor) return launch_one<FC1, DT, NB, BITS, kZpTensor, true>(p, plan, s);
-        return staged ? launch_one<FC1, DT, NB, BITS, kZpConst, true, true>(p, plan, s)
-                      : launch_one<FC1, DT, NB, BITS, kZpConst, true>(p, plan, s);
+    // the staged scale table covers contiguous weight rows: interleaved fc1 only
+    const bool staged = zp != kZpTensor && can_stage(p) && (!FC1 || p.fusion == 1);
+    // raw codes: 2/3/4-bit (8-bit codes overflow the bf16 raw bias's exact range)
+    constexpr bool kRawOk = BITS == 2 || BITS == 3 || BITS == 4;
+    if constexpr (kRawOk) {
+        if (p.block_size % kSuperK == 0) {  // zero point applied in float32: any value works
+            if (zp == kZpTensor) return launch_one<FC1, DT, NB, BITS, kZpTensor, true>(p, plan, s);
+            return staged ? launch_one<FC1, DT, NB, BITS, kZpConst, true, true>(p, plan, s)
+                          : launch_one<FC1, DT, NB, BITS, kZpConst, true>(p, plan, s);
+        }
     }
     if (zp == kZpTensor) return launch_one<FC1, DT, NB, BITS, kZpTensor, false>(p, plan, s);
     if (zp == kZpConst && staged) {
@@ -790,8 +816,13 @@ hipError_t launch_dt(const ProjLaunch& p, const DecodePlan* plan, hipStream_t s)
     case 2: return launch_zp<FC1, DT, NB, 2>(p, plan, s);
     case 3: return launch_zp<FC1, DT, NB, 3>(p, plan, s);
     case 4: return launch_zp<FC1, DT, NB, 4>(p, plan, s);
-    default: return hipErrorInvalidValue;
+    default: break;
     }
+    if (plan == nullptr) {  // 1- and 8-bit codes: the m-tile kernels only
+        if (p.w.bits == 1) return launch_zp<FC1, DT, NB, 1>(p, plan, s);
+        if (p.w.bits == 8) return launch_zp<FC1, DT, NB, 8>(p, plan, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -103,33 +103,58 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
         // reads the expert's first rows and stores nothing
         int col0;  // fc1: first activation column of this wave; fc2: first hidden column
         bool active;
-        uint32_t wrow[4];  // weight row within the expert
+        uint32_t wrow[4];  // weight row within the expert's tensor of column block nb
+        // fc1 column blocks 0 and 2 are gate rows of activation columns col0 + c
+        // and col0 + 16 + c, blocks 1 and 3 their up rows, placed by the gate/up
+        // layout (interleaved, halves, or the separate fc3 tensor)
+        const int fusion = FC1 ? p.fusion : 1;
+        const int I = p.N / 2;
         if constexpr (FC1) {
             col0 = ntile * (kRows / 2) + wave * 32;
-            active = col0 < p.N / 2;
-            const uint32_t base = active ? 2 * (col0 + c) : 0;
-            wrow[0] = base;
-            wrow[1] = base + 1;
-            wrow[2] = base + (active ? 32 : 0);
-            wrow[3] = base + (active ? 33 : 1);
+            active = col0 < I;
+            const int j0 = active ? col0 + c : 0, j1 = active ? col0 + 16 + c : 0;
+            wrow[0] = (uint32_t)fc1_row(fusion, j0, false, I);
+            wrow[1] = (uint32_t)fc1_row(fusion, j0, true, I);
+            wrow[2] = (uint32_t)fc1_row(fusion, j1, false, I);
+            wrow[3] = (uint32_t)fc1_row(fusion, j1, true, I);
         } else {
             col0 = ntile * kRows + wave * 64;
             active = col0 < p.N;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) wrow[nb] = active ? col0 + nb * 16 + c : 0;
         }
-        const int64_t erow = (int64_t)e * p.N;
+        // rows per expert of the (first) tensor: fc1 holds only the gate rows when fc3 holds the up rows
+        const int64_t rows_e = (FC1 && fusion == 0) ? I : p.N;
+        const int64_t erow = (int64_t)e * rows_e;
         const uint8_t* codes_e = p.w.codes + erow * row_bytes;
         const uint16_t* scales_e = reinterpret_cast<const uint16_t*>(p.w.scales) + erow * n_blocks;
         const uint8_t* zp_e = ZP == kZpTensor ? p.w.zp + erow * zp_bytes : nullptr;
+        const bool sep = FC1 && fusion == 0;  // up rows from fc3 (same width, block size and zp mode)
+        const uint8_t* codes_u = sep ? p.w3.codes + erow * row_bytes : codes_e;
+        const uint16_t* scales_u = sep ? reinterpret_cast<const uint16_t*>(p.w3.scales) + erow * n_blocks : scales_e;
+        const uint8_t* zp_u = (ZP == kZpTensor && sep) ? p.w3.zp + erow * zp_bytes : zp_e;
+        const uint8_t* codes_nb[4] = {codes_e, codes_u, codes_e, codes_u};
+        const uint16_t* scales_nb[4] = {scales_e, scales_u, scales_e, scales_u};
+        const uint8_t* zp_nb[4] = {zp_e, zp_u, zp_e, zp_u};
 
-        // STAGED: lane l loads row l of the wavefront's 64 contiguous weight
-        // rows (fc1: 2*col0.., fc2: col0..) into slot l; fc1 slots are
-        // interleaved so that the rows a load of column block nb reads sit in
-        // 16 consecutive slots (no LDS bank conflicts).
-        const uint32_t wr_base = active ? (FC1 ? 2 * col0 : col0) : 0;
-        const uint16_t* sc_row = scales_e + (wr_base + lane) * n_blocks;
-        const int sc_slot_store = FC1 ? ((lane >> 1) | ((lane & 1) << 5)) : lane;
+        // STAGED: lane l loads the scales of one of the wavefront's 64 weight
+        // rows into slot l: fc2 rows col0 + l; fc1 with interleaved rows
+        // 2*col0 + l, slots interleaved so that the rows a load of column
+        // block nb reads sit in 16 consecutive slots (no LDS bank conflicts);
+        // fc1 with the other layouts the gate rows of columns col0 + l (l < 32)
+        // and the up rows of columns col0 + l - 32.
+        const uint16_t* sc_row;
+        int sc_slot_store;
+        if (FC1 && fusion != 1) {
+            const int jl = active ? col0 + (lane & 31) : 0;
+            const bool up = lane >= 32;
+            sc_row = (up ? scales_u : scales_e) + fc1_row(fusion, jl, up, I) * n_blocks;
+            sc_slot_store = lane;
+        } else {
+            const uint32_t wr_base = active ? (FC1 ? 2 * col0 : col0) : 0;
+            sc_row = scales_e + (wr_base + lane) * n_blocks;
+            sc_slot_store = FC1 ? ((lane >> 1) | ((lane & 1) << 5)) : lane;
+        }
         const int stage_end = s_end >> ss_shift;  // parts hold whole stages
         u32x4 sc_next;
         auto stage_load = [&](int stage) { sc_next = *reinterpret_cast<const u32x4*>(sc_row + 8 * stage); };
@@ -179,11 +204,11 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
                 constexpr int kSlot[4] = {0, FC1 ? 32 : 16, FC1 ? 16 : 32, 48};
                 q.scale = sc_lds[wave][(c + kSlot[nb]) * 8 + (q.blk & 7)];
             } else {
-                q.scale = scales_e[wrow[nb] * n_blocks + q.blk];
+                q.scale = scales_nb[nb][wrow[nb] * n_blocks + q.blk];
             }
             q.zp = 0;
             if constexpr (ZP == kZpTensor) {
-                q.zp = zp_e[wrow[nb] * zp_bytes + (BITS == 3 ? q.blk : q.blk >> (BITS == 2 ? 2 : 1))];
+                q.zp = zp_nb[nb][wrow[nb] * zp_bytes + (BITS == 3 ? q.blk : q.blk / (8 / BITS))];
             }
             return q;
         };
@@ -198,7 +223,7 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
             }
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
-                sp[nb] = load_span<BITS>(codes_e + wrow[nb] * row_bytes, kk);
+                sp[nb] = load_span<BITS>(codes_nb[nb] + wrow[nb] * row_bytes, kk);
                 bp[nb] = params(nb, kk);
             }
         };
@@ -282,6 +307,25 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
         }
 
         if (!active) continue;
+        // expert biases of this lane's four output columns [qmoe.rs,
+        // qmoe_linear_impl: the bias entry of (expert, output row) is added to
+        // the float32 projection output]; fc2 adds its bias in K part 0 only
+        float bias_v[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (FC1) {
+            const int js[2] = {col0 + c, col0 + 16 + c};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (p.bias) bias_v[2 * h] = p.bias[erow + fc1_row(fusion, js[h], false, I)];
+                if (sep) {
+                    if (p.bias3) bias_v[2 * h + 1] = p.bias3[erow + js[h]];
+                } else if (p.bias) {
+                    bias_v[2 * h + 1] = p.bias[erow + fc1_row(fusion, js[h], true, I)];
+                }
+            }
+        } else if (p.bias && ks == 0) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) bias_v[nb] = p.bias[erow + col0 + nb * 16 + c];
+        }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -289,15 +333,15 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
                 const int m = mb * 16 + 4 * g + i;
                 if (m >= rows) continue;
                 if constexpr (FC1) {
-                    const int I = p.N / 2;
                     uint16_t* out = reinterpret_cast<uint16_t*>(p.act_out) + (int64_t)(row0 + m) * I;
-                    out[col0 + c] = Dt<DT>::from_float(act_value<DT>(p.act, acc[mb][0][i], acc[mb][1][i]));
-                    out[col0 + 16 + c] =
-                        Dt<DT>::from_float(act_value<DT>(p.act, acc[mb][2][i], acc[mb][3][i]));
+                    out[col0 + c] = Dt<DT>::from_float(
+                        act_value<DT>(p.act, acc[mb][0][i] + bias_v[0], acc[mb][1][i] + bias_v[1], p.ap));
+                    out[col0 + 16 + c] = Dt<DT>::from_float(
+                        act_value<DT>(p.act, acc[mb][2][i] + bias_v[2], acc[mb][3][i] + bias_v[3], p.ap));
                 } else {
                     float* out = p.y2 + ks * p.part_stride + (int64_t)row_dst[m] * p.N;
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) out[col0 + nb * 16 + c] = acc[mb][nb][i];
+                    for (int nb = 0; nb < 4; ++nb) out[col0 + nb * 16 + c] = acc[mb][nb][i] + bias_v[nb];
                 }
             }
         }
@@ -382,8 +426,13 @@ hipError_t launch_bits(const ProjLaunch& p, hipStream_t s)
     case 2: return launch_zp<FC1, DT, 2, MT>(p, s);
     case 3: return launch_zp<FC1, DT, 3, MT>(p, s);
     case 4: return launch_zp<FC1, DT, 4, MT>(p, s);
-    default: return hipErrorInvalidValue;
+    default: break;
     }
+    if constexpr (MT == kPrefillMTSmall) {  // 1- and 8-bit codes take the small tile
+        if (p.w.bits == 1) return launch_zp<FC1, DT, 1, MT>(p, s);
+        if (p.w.bits == 8) return launch_zp<FC1, DT, 8, MT>(p, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <bool FC1>

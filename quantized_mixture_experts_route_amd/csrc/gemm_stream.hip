@@ -452,7 +452,7 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
             if (m < count && c < 8) {
                 const int I = p.N / 2;
                 uint16_t* out = act_out + (int64_t)(first + m) * I;
-                out[col0 + c] = Dt<DT>::from_float(act_value<DT>(act, sum[i], up));
+                out[col0 + c] = Dt<DT>::from_float(act_value<DT>(act, sum[i], up, p.ap));
             }
         } else {
             if (m < count) store_y2(&y2[(int64_t)y2_row[i] * p.N + col0 + c], sum[i], p.fused.counters != nullptr);

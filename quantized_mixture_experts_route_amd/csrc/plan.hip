@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(
     const float* __restrict__ logits, int T, int E, int top_k, int normalize,
     float* __restrict__ weights, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
     int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles, int32_t* __restrict__ counters,
-    int n_counters)
+    int n_counters, const float* __restrict__ agg)
 {
     __shared__ __attribute__((aligned(16))) int s_e[kDecodeMaxRoutes];  // expert of route r
     __shared__ int s_route[kDecodeMaxRoutes];  // route at sorted position p
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(
             weights[r] = w;
             if (ids_out) ids_out[r] = e;
             if (w_out) w_out[r] = w;
-        });
+        }, agg ? agg + (int64_t)t * E : nullptr);
     }
     __syncthreads();
 
@@ -131,10 +131,10 @@ __global__ __launch_bounds__(kThreads) void decode_plan_kernel(
 template <int EPL>
 hipError_t launch_epl(const float* logits, int T, int E, int top_k, int normalize, float* weights,
                   int32_t* ids_out, float* w_out, int32_t* tiles, int32_t* n_tiles,
-                  int32_t* counters, int n_counters, hipStream_t s)
+                  int32_t* counters, int n_counters, const float* agg, hipStream_t s)
 {
     launch(decode_plan_kernel<EPL>, dim3(1), dim3(kThreads), s, logits, T, E, top_k,
-                       normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters);
+                       normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, agg);
     return hipGetLastError();
 }
 
@@ -142,15 +142,16 @@ hipError_t launch_epl(const float* logits, int T, int E, int top_k, int normaliz
 
 hipError_t launch_decode_plan(const float* logits, int T, int E, int top_k, int normalize,
                               float* weights, int32_t* ids_out, float* w_out, int32_t* tiles,
-                              int32_t* n_tiles, int32_t* counters, int n_counters, hipStream_t s)
+                              int32_t* n_tiles, int32_t* counters, int n_counters, hipStream_t s,
+                              const float* agg)
 {
     if (T < 1 || T * top_k > kDecodeMaxRoutes) return hipErrorInvalidValue;
     const int epl = (E + kWave - 1) / kWave;
-    if (epl <= 1) return launch_epl<1>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, s);
-    if (epl <= 2) return launch_epl<2>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, s);
-    if (epl <= 4) return launch_epl<4>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, s);
-    if (epl <= 8) return launch_epl<8>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, s);
-    return launch_epl<16>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, s);
+    if (epl <= 1) return launch_epl<1>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, agg, s);
+    if (epl <= 2) return launch_epl<2>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, agg, s);
+    if (epl <= 4) return launch_epl<4>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, agg, s);
+    if (epl <= 8) return launch_epl<8>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, agg, s);
+    return launch_epl<16>(logits, T, E, top_k, normalize, weights, ids_out, w_out, tiles, n_tiles, counters, n_counters, agg, s);
 }
 
 }  // namespace qmoe

@@ -215,11 +215,8 @@ bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L,
 
 int check_bits(const char* name, int bits)
 {
-    if (bits == 2 || bits == 3 || bits == 4) return QMOE_OK;
-    if (bits == 1 || bits == 8) {
-        return fail(QMOE_ERR_UNSUPPORTED, "%s bits=%d: only 2, 3 and 4 have kernels", name, bits);
-    }
-    return fail(QMOE_ERR_INVALID_ARG, "%s bits=%d is not a weight width", name, bits);
+    if (bits == 1 || bits == 2 || bits == 3 || bits == 4 || bits == 8) return QMOE_OK;
+    return fail(QMOE_ERR_INVALID_ARG, "%s bits=%d is not a weight width (1, 2, 3, 4 or 8)", name, bits);
 }
 
 int check_proj(const char* name, const qmoe_proj* p)
@@ -376,7 +373,22 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
                  int32_t dtype, void* out, int32_t* topk_ids_out, float* topk_w_out,
                  void* workspace, size_t workspace_bytes, void* stream)
 {
+    return qmoe_forward_ex(hidden, logits, T, H, I, E, fc1, fc2, zero_point_offset, block_size,
+                           top_k, normalize, activation, dtype, out, topk_ids_out, topk_w_out,
+                           nullptr, workspace, workspace_bytes, stream);
+}
+
+int qmoe_forward_ex(const void* hidden, const float* logits, int64_t T, int32_t H, int32_t I,
+                    int32_t E, const qmoe_proj* fc1, const qmoe_proj* fc2, float zero_point_offset,
+                    int32_t block_size, int32_t top_k, int32_t normalize, int32_t activation,
+                    int32_t dtype, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                    const qmoe_layer_opts* opts, void* workspace, size_t workspace_bytes,
+                    void* stream)
+{
     int rc;
+    const qmoe_layer_opts defaults = {nullptr, nullptr, nullptr, nullptr, nullptr,
+                                      QMOE_SWIGLU_INTERLEAVED, 1.0f, 0.0f, INFINITY};
+    const qmoe_layer_opts& o = opts ? *opts : defaults;
     if (T < 0) return fail(QMOE_ERR_INVALID_ARG, "T=%lld < 0", (long long)T);
     if (H <= 0 || I <= 0) return fail(QMOE_ERR_INVALID_ARG, "H=%d and I=%d must be > 0", H, I);
     if (E < 1 || E > 1024) return fail(QMOE_ERR_INVALID_ARG, "E=%d outside [1, 1024]", E);
@@ -398,6 +410,33 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     if (H % qmoe::kSuperK || I % qmoe::kSuperK) {
         return fail(QMOE_ERR_UNSUPPORTED, "H=%d and I=%d must be multiples of %d", H, I, qmoe::kSuperK);
     }
+    // operator options [qmoe.rs: swiglu_fusion in {0, 1, 2}, only with SwiGLU;
+    // fc3 exactly when the gate is separate; biases, router_weights optional]
+    if (o.swiglu_fusion < 0 || o.swiglu_fusion > 2) {
+        return fail(QMOE_ERR_INVALID_ARG, "swiglu_fusion=%d must be 0, 1 or 2", o.swiglu_fusion);
+    }
+    if (o.swiglu_fusion != QMOE_SWIGLU_INTERLEAVED && activation != QMOE_ACT_SWIGLU) {
+        return fail(QMOE_ERR_INVALID_ARG, "swiglu_fusion=%d is only valid with SWIGLU", o.swiglu_fusion);
+    }
+    if ((o.swiglu_fusion == QMOE_SWIGLU_SEPARATE) != (o.fc3 != nullptr)) {
+        return fail(QMOE_ERR_INVALID_ARG, "fc3 is required exactly when swiglu_fusion = 0");
+    }
+    if (o.fc3) {
+        if ((rc = check_proj("fc3", o.fc3))) return rc;
+        if (o.fc3->bits != fc1->bits || (o.fc3->zero_points == nullptr) != (fc1->zero_points == nullptr)) {
+            return fail(QMOE_ERR_UNSUPPORTED, "fc3 must have fc1's width and zero-point mode");
+        }
+    }
+    if (o.fc3_bias && !o.fc3) return fail(QMOE_ERR_INVALID_ARG, "fc3_bias without fc3");
+    if ((o.fc1_bias && !aligned(o.fc1_bias, 4)) || (o.fc2_bias && !aligned(o.fc2_bias, 4)) ||
+        (o.fc3_bias && !aligned(o.fc3_bias, 4)) || (o.router_weights && !aligned(o.router_weights, 4))) {
+        return fail(QMOE_ERR_INVALID_ARG, "biases and router_weights must be 4-byte aligned");
+    }
+    // layers with biases, another gate/up layout, router_weights or 1/8-bit codes
+    // take the generic kernels (prefill tiles, decode plan + m-tile kernels)
+    const bool wide_codes = fc1->bits == 1 || fc1->bits == 8 || fc2->bits == 1 || fc2->bits == 8;
+    const bool generic = wide_codes || o.swiglu_fusion != QMOE_SWIGLU_INTERLEAVED || o.fc1_bias ||
+                         o.fc2_bias || o.router_weights;
     Layout L;
     if (!make_layout(T, H, I, E, top_k, &L)) return fail(QMOE_ERR_INVALID_ARG, "sizes overflow");
     if (T == 0) return ok();
@@ -408,7 +447,7 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     const qmoe::ProjArgs w2 = proj_args(fc2, zero_point_offset);
     const bool stageable = (H / block_size) % 8 == 0 && (I / block_size) % 8 == 0 &&
                            aligned(w1.scales, 16) && aligned(w2.scales, 16);
-    if (!L.decode && block_size >= 32 && w1.fast && w2.fast && stageable &&
+    if (!L.decode && block_size >= 32 && w1.fast && w2.fast && stageable && !wide_codes &&
         (T * top_k / qmoe::kPrefillMTLarge) * ceil_div(I, qmoe::prefill_fc1_cols(qmoe::kPrefillMTLarge)) >= 1024) {
         make_layout(T, H, I, E, top_k, &L, qmoe::kPrefillMTLarge);
     }
@@ -460,10 +499,10 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     // Streamed decode (at most 16 tokens and 64 routes): the same idea with every
     // wavefront owning whole weight rows and consuming its weights piece by
     // piece as they arrive.
-    const bool stream_mode = L.decode && T <= 16 && R <= 64 && E <= 64 && E <= R &&
+    const bool stream_mode = !generic && L.decode && T <= 16 && R <= 64 && E <= 64 && E <= R &&
                              qmoe::stream_fits(w1, H, 2 * I, block_size, true) &&
                              qmoe::stream_fits(w2, I, H, block_size, false);
-    const bool expert_mode = !stream_mode && L.decode && E <= 64 && E <= R && H <= 2048 &&
+    const bool expert_mode = !generic && !stream_mode && L.decode && E <= 64 && E <= R && H <= 2048 &&
                              I <= 2048 && fc1->bits == 2 && fc1->zero_points == nullptr;
     // The combine folds into fc2 on the streamed path only: there a column
     // block's few expert workgroups finish together; the m-tile and
@@ -481,17 +520,17 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     // per token, so a tile holds at most min(T, 16) rows.
     const bool list_mode = L.decode && !expert_mode && !stream_mode;
     const int max_rows = (int)(T < qmoe::kDecodeMT ? T : qmoe::kDecodeMT);
-    const bool rows1 = list_mode && qmoe::rows_fits(w1, H, 2 * I, block_size);
-    const bool rows2 = list_mode && qmoe::rows_fits(w2, I, H, block_size);
+    const bool rows1 = list_mode && !generic && qmoe::rows_fits(w1, H, 2 * I, block_size);
+    const bool rows2 = list_mode && !generic && qmoe::rows_fits(w2, I, H, block_size);
     if (L.decode && !expert_mode && !stream_mode) {  // routing, grouping and the m-tile list in one launch
         timer_begin(QMOE_STAGE_ROUTE, s);
         e = qmoe::launch_decode_plan(logits, (int)T, E, top_k, normalize, w, topk_ids_out,
-                                     topk_w_out, wl1, n1, counters, n_counters, s);
+                                     topk_w_out, wl1, n1, counters, n_counters, s, o.router_weights);
         timer_end(QMOE_STAGE_ROUTE, s);
         if (e != hipSuccess) return hip_fail(e, "decode plan launch");
     } else if (!L.decode) {
         timer_begin(QMOE_STAGE_ROUTE, s);
-        e = qmoe::launch_route(logits, T, E, top_k, normalize, ids, w, s);
+        e = qmoe::launch_route(logits, T, E, top_k, normalize, ids, w, s, o.router_weights);
         timer_end(QMOE_STAGE_ROUTE, s);
         if (e != hipSuccess) return hip_fail(e, "route launch");
 
@@ -518,6 +557,11 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     p1.tiles_cap = L.m_tiles;
     p1.act = activation;
     p1.act_out = act;
+    p1.ap = qmoe::ActParams{o.activation_alpha, o.activation_beta, o.swiglu_limit};
+    p1.fusion = o.swiglu_fusion;
+    if (o.fc3) p1.w3 = proj_args(o.fc3, zero_point_offset);
+    p1.bias = o.fc1_bias;
+    p1.bias3 = o.fc3_bias;
     timer_begin(QMOE_STAGE_FC1, s);
     e = stream_mode ? qmoe::launch_fc1_stream(p1, plan, dtype, s)
         : rows1     ? qmoe::launch_rows_decode(p1, true, max_rows, dtype, s)
@@ -543,6 +587,7 @@ int qmoe_forward(const void* hidden, const float* logits, int64_t T, int32_t H, 
     p2.y2 = y2;
     p2.k_split = k_split;
     p2.part_stride = R * (int64_t)H;
+    p2.bias = o.fc2_bias;
     p2.fused = qmoe::FusedCombine{counters, w, out, (int)T};  // decode: fc2 combines (counters set)
     timer_begin(QMOE_STAGE_FC2, s);
     e = stream_mode ? qmoe::launch_fc2_stream(p2, plan, dtype, s)
@@ -692,6 +737,9 @@ int qmoe_raw_codes(const qmoe_proj* p, int32_t E, int32_t N, int32_t K, int32_t 
     }
     if (variant == QMOE_RAW_MULTI_BASE && p->bits == 3) {
         return fail(QMOE_ERR_UNSUPPORTED, "the multi-base raw codes take 2- and 4-bit codes only");
+    }
+    if (p->bits == 1 || p->bits == 8) {
+        return fail(QMOE_ERR_UNSUPPORTED, "no kernel feeds raw %d-bit codes to the matrix cores", p->bits);
     }
     if (!codes_out || !aligned(codes_out, 4)) return fail(QMOE_ERR_INVALID_ARG, "codes_out must be non-NULL");
     int64_t rows, elems;

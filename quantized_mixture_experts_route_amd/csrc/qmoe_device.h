@@ -96,6 +96,13 @@ __device__ inline Span<BITS> load_span(const uint8_t* row, int k0)
     } else if constexpr (BITS == 2) {
         const uint2 v = *reinterpret_cast<const uint2*>(p);
         s.w[0] = v.x; s.w[1] = v.y;
+    } else if constexpr (BITS == 8) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
+        s.w[0] = a.x; s.w[1] = a.y; s.w[2] = a.z; s.w[3] = a.w;
+        s.w[4] = b.x; s.w[5] = b.y; s.w[6] = b.z; s.w[7] = b.w;
+    } else if constexpr (BITS == 1) {
+        s.w[0] = *reinterpret_cast<const uint32_t*>(p);
     } else {
         const uint3 v = *reinterpret_cast<const uint3*>(p);
         s.w[0] = v.x; s.w[1] = v.y; s.w[2] = v.z;
@@ -185,6 +192,8 @@ __device__ inline uint32_t span_code(const Span<BITS>& s, int c)
 {
     if constexpr (BITS == 4) return (s.w[c >> 3] >> (4 * (c & 7))) & 15u;
     else if constexpr (BITS == 2) return (s.w[c >> 4] >> (2 * (c & 15))) & 3u;
+    else if constexpr (BITS == 8) return (s.w[c >> 2] >> (8 * (c & 3))) & 255u;
+    else if constexpr (BITS == 1) return (s.w[0] >> c) & 1u;
     else return (span_group<3>(s, c >> 3) >> (3 * (c & 7))) & 7u;
 }
 
@@ -341,6 +350,24 @@ __device__ inline u32x4 dequant_step(const Span<BITS>& sp, int t, float zp, floa
             for (int r = 0; r < 4; ++r) {
                 const int j = j0 + r;
                 raw[r] = and_or(j == 0 ? (w << 1) : (w >> (2 * j - 1)), 0x00060006u, kMagic);
+            }
+        } else if constexpr (BITS == 8) {
+            // register r pairs bytes 8t + r and 8t + r + 4 (kStride4): one
+            // v_perm_b32 places them at bits 0 and 16 with zero bytes beside them
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t sel = (uint32_t)r | 0x0c00u | ((uint32_t)(4 + r) << 16) | 0x0c000000u;
+                const uint32_t y = __builtin_amdgcn_perm(sp.w[2 * t + 1], sp.w[2 * t], sel);
+                raw[r] = and_or(y << 1, 0x01fe01feu, kMagic);
+            }
+        } else if constexpr (BITS == 1) {
+            // register r pairs bits 8t + r and 8t + r + 4 of the span's word
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // only bits 0 and 4 survive the mask, so the spread copies
+                // (bit 0 to 1, bit 4 to 17) cannot collide with other codes
+                const uint32_t x = (sp.w[0] >> (8 * t + r)) & 0x11u;
+                raw[r] = and_or((x | (x << 12)) << 1, 0x00020002u, kMagic);
             }
         } else {
             const uint32_t g = span_group<3>(sp, t);

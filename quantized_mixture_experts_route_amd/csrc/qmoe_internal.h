@@ -83,6 +83,13 @@ struct FusedCombine {
     int T;
 };
 
+// Gated-activation parameters (SwiGLU alpha, beta, limit).
+struct ActParams {
+    float alpha = 1.0f;
+    float beta = 0.0f;
+    float limit = __builtin_inff();
+};
+
 // One grouped projection over a work-list.
 struct ProjLaunch {
     const void* a;            // fc1: hidden [T, K]; fc2: activations [R, K] in sorted order
@@ -104,6 +111,12 @@ struct ProjLaunch {
     int k_split;              // prefill fc2: K parts (1, 2 or 4), each a work-list column block
     int64_t part_stride;      // prefill fc2: floats between the parts of y2
     FusedCombine fused;       // decode fc2: the combine folded in (counters nullable)
+    // operator options (prefill and m-tile decode kernels only)
+    ActParams ap;             // fc1: SwiGLU parameters
+    int fusion = 1;           // fc1 gate/up layout: 1 interleaved, 2 halves, 0 separate fc3
+    ProjArgs w3{};            // fc1 with fusion 0: the up projection [E, I, K]
+    const float* bias = nullptr;   // nullable: fc1 [E, rows of fc1] / fc2 [E, N]
+    const float* bias3 = nullptr;  // nullable: fc3 [E, I]
 };
 
 // Routing inputs and outputs of the expert-stationary decode kernels: fc1
@@ -122,8 +135,9 @@ struct DecodePlan {
     int n_counters;
 };
 
+// agg: NULL or router_weights [T, E] (the weights of the selected experts)
 hipError_t launch_route(const float* logits, int64_t T, int E, int top_k, int normalize,
-                        int32_t* ids, float* weights, hipStream_t s);
+                        int32_t* ids, float* weights, hipStream_t s, const float* agg = nullptr);
 
 // Router projection + top-k (router.hip): logits = hidden @ gate_weight^T in
 // float32 on the matrix cores, then route_values on them.
@@ -146,7 +160,8 @@ hipError_t launch_group(const int32_t* ids, int R, int E, int m_tile, int nt1, i
 // kDecodeMaxRoutes).  ids_out / w_out may be NULL.
 hipError_t launch_decode_plan(const float* logits, int T, int E, int top_k, int normalize,
                               float* weights, int32_t* ids_out, float* w_out, int32_t* tiles,
-                              int32_t* n_tiles, int32_t* counters, int n_counters, hipStream_t s);
+                              int32_t* n_tiles, int32_t* counters, int n_counters, hipStream_t s,
+                              const float* agg = nullptr);
 
 hipError_t launch_fc1_prefill(const ProjLaunch& p, int dtype, hipStream_t s);
 hipError_t launch_fc2_prefill(const ProjLaunch& p, int dtype, hipStream_t s);

@@ -34,9 +34,14 @@ __device__ inline float key_to_logit(int32_t key)
 // logit of expert lane + 64 j; it is called once for every j < EPL, also where
 // lane + 64 j >= E (the value is then ignored), so that all of a lane's loads
 // are issued before the first one is waited on.  For every slot s < top_k
-// exactly one lane calls emit(s, expert, weight).
+// exactly one lane calls emit(s, expert, weight).  agg: NULL, or the token's
+// row of aggregation weights [qmoe.rs, qmoe_route, its router_weights
+// branch]: the logits then only select, and a selected expert's weight is
+// agg[e], divided by the slot-order sum of the selected agg values when
+// normalize is set (0 when that sum is 0).
 template <int EPL, class Get, class Emit>
-__device__ inline void route_values(int E, int top_k, int normalize, Get get, Emit emit)
+__device__ inline void route_values(int E, int top_k, int normalize, Get get, Emit emit,
+                                    const float* agg = nullptr)
 {
     const int lane = threadIdx.x & (kWave - 1);
     float val[EPL];
@@ -73,7 +78,7 @@ __device__ inline void route_values(int E, int top_k, int normalize, Get get, Em
         best = wave_max_keyed(best);  // words are distinct: each holds its expert index
         const int e = (int)~(uint32_t)best;
         const float v = key_to_logit((int32_t)((uint32_t)(best >> 32) ^ 0x80000000u));
-        const float num = expf(v - m);
+        const float num = agg ? agg[e] : expf(v - m);
         if (normalize) {
             den += num;  // slot order
         }
@@ -88,7 +93,9 @@ __device__ inline void route_values(int E, int top_k, int normalize, Get get, Em
             }
         }
     }
-    if (!normalize) {
+    if (agg && !normalize) {
+        den = 1.0f;
+    } else if (!normalize) {
         float part = 0.0f;
 #pragma unroll
         for (int j = 0; j < EPL; ++j) {
@@ -103,17 +110,19 @@ __device__ inline void route_values(int E, int top_k, int normalize, Get get, Em
     for (int j = 0; j < EPL; ++j) {
         const int s = lane + kWave * j;
         if (s < top_k) {
-            emit(s, my_id[j], my_num[j] / den);
+            emit(s, my_id[j], (agg && den == 0.0f) ? 0.0f : my_num[j] / den);
         }
     }
 }
 
 // Routes the token whose E logits start at `row`.
 template <int EPL, class Emit>
-__device__ inline void route_token(const float* row, int E, int top_k, int normalize, Emit emit)
+__device__ inline void route_token(const float* row, int E, int top_k, int normalize, Emit emit,
+                                   const float* agg = nullptr)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    route_values<EPL>(E, top_k, normalize, [&](int j) { return row[min(lane + kWave * j, E - 1)]; }, emit);
+    route_values<EPL>(E, top_k, normalize, [&](int j) { return row[min(lane + kWave * j, E - 1)]; }, emit,
+                      agg);
 }
 
 }  // namespace qmoe

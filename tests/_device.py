@@ -62,3 +62,27 @@ def as_f64(t: torch.Tensor) -> np.ndarray:
 
 def nan_to(x):
     return math.nan if x is None else x
+
+
+def option_kwargs(inp: dict, spec: dict, device="cuda") -> dict:
+    """qm.forward keyword options (device tensors) for the operator options in spec/inp."""
+    kw = {}
+    fusion = spec.get("swiglu_fusion", 1)
+    if fusion != 1:
+        kw["swiglu_fusion"] = fusion
+    if fusion == 0:
+        zp = inp.get("fc3_zp")
+        kw["fc3"] = qm.Projection(
+            codes=torch.from_numpy(inp["fc3_codes"]).to(device),
+            scales=bits_tensor(inp["fc3_scales"], spec["dtype"], device),
+            zero_points=None if zp is None else torch.from_numpy(zp).to(device),
+            bits=spec.get("fc3_bits", spec["fc1_bits"]))
+    for name in ("fc1_bias", "fc2_bias", "fc3_bias", "router_weights"):
+        if inp.get(name) is not None:
+            kw[name] = torch.from_numpy(inp[name]).to(device)
+    for key, arg in (("alpha", "activation_alpha"), ("beta", "activation_beta"),
+                     ("limit", "swiglu_limit")):
+        if key in spec:
+            kw[arg] = spec[key]
+    return kw
+

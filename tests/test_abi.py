@@ -104,8 +104,8 @@ INVALID_FORWARD = [
     (dict(H=272, bs=32), qm.ERR_INVALID_ARG),
     (dict(H=160, bs=32), qm.ERR_UNSUPPORTED),
     (dict(I=96, bs=32), qm.ERR_UNSUPPORTED),
-    (dict(fc1=_proj(bits=8)), qm.ERR_UNSUPPORTED),
-    (dict(fc2=_proj(bits=1)), qm.ERR_UNSUPPORTED),
+    (dict(fc1=_proj(bits=5)), qm.ERR_INVALID_ARG),
+    (dict(fc2=_proj(bits=6)), qm.ERR_INVALID_ARG),
     (dict(fc2=_proj(bits=5)), qm.ERR_INVALID_ARG),
     (dict(fc1=None), qm.ERR_INVALID_ARG),
     (dict(fc1=_proj(codes=None)), qm.ERR_INVALID_ARG),
@@ -127,6 +127,39 @@ def test_forward_rejects_before_launch(kw, code):
     rc = _fwd(lib, **kw)
     assert rc == code, (kw, rc, qm.last_error())
     assert qm.last_error().startswith("qmoe: ")
+
+
+def _opts(**kw):
+    o = qm._LayerOpts(None, None, None, None, None, qm.SWIGLU_INTERLEAVED, 1.0, 0.0, math.inf)
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def test_forward_ex_option_validation():
+    lib = qm.load_library()
+    p = _proj()
+    p3 = _proj(bits=2)
+
+    def call(opts, act=0):
+        return lib.qmoe_forward_ex(FAKE, FAKE, 4, 256, 256, 8, ctypes.byref(p), ctypes.byref(p),
+                                   math.nan, 32, 2, 1, act, 1, FAKE, None, None, ctypes.byref(opts),
+                                   FAKE, 1 << 30, None)
+
+    assert call(_opts(swiglu_fusion=3)) == qm.ERR_INVALID_ARG
+    assert call(_opts(swiglu_fusion=2), act=1) == qm.ERR_INVALID_ARG  # halves only with SwiGLU
+    assert call(_opts(swiglu_fusion=0)) == qm.ERR_INVALID_ARG          # fc3 missing
+    assert call(_opts(fc3=ctypes.pointer(p))) == qm.ERR_INVALID_ARG    # fc3 without fusion 0
+    assert call(_opts(swiglu_fusion=0, fc3=ctypes.pointer(p3))) == qm.ERR_UNSUPPORTED  # width
+    assert call(_opts(fc3_bias=FAKE)) == qm.ERR_INVALID_ARG            # fc3_bias without fc3
+    assert call(_opts(fc1_bias=FAKE + 2)) == qm.ERR_INVALID_ARG        # alignment
+    assert call(_opts(router_weights=FAKE + 1)) == qm.ERR_INVALID_ARG
+    # T = 0 with every option set is a no-op
+    opts = _opts(swiglu_fusion=0, fc3=ctypes.pointer(p), fc1_bias=FAKE, fc2_bias=FAKE,
+                 fc3_bias=FAKE, router_weights=FAKE, activation_alpha=1.7, swiglu_limit=7.0)
+    assert lib.qmoe_forward_ex(None, None, 0, 256, 256, 8, ctypes.byref(p), ctypes.byref(p),
+                               math.nan, 32, 2, 1, 0, 1, None, None, None, ctypes.byref(opts),
+                               None, 0, None) == qm.OK
 
 
 def test_forward_zero_tokens_is_a_noop():
