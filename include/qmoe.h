@@ -168,7 +168,9 @@ int qmoe_group(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int
  * weights, fc1 and activation rows, route outputs, grouping arrays) from the
  * shapes alone; moe.rs, the MoE workspace estimator].  The layout depends on
  * neither the weight widths nor block_size, so unlike those estimators this
- * takes no bits or block_size argument. */
+ * takes no bits or block_size argument.  It never decreases as T grows (the
+ * other sizes fixed), so a workspace sized for the largest batch serves every
+ * smaller one. */
 size_t qmoe_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t top_k,
                            int32_t dtype);
 

@@ -150,8 +150,28 @@ int fc2_split(int64_t R, int E, int H, int I, int mt)
     return best;
 }
 
+// Routes above which no prefill layer splits fc2's K: a split pays only
+// while the fc2 items need fewer than 10 rounds of the persistent grid (at 10
+// or more, no S saves a tenth of the makespan), and the items grow with
+// ceil(R / m_tile) per column block.
+int64_t split_route_limit(int H)
+{
+    int64_t lim = 0;
+    for (int mt : {qmoe::kPrefillMTSmall, qmoe::kPrefillMTLarge}) {
+        const int64_t nt = ceil_div(H, qmoe::prefill_fc2_cols(mt));
+        const int64_t slots = 256 * (mt == qmoe::kPrefillMTLarge ? 1 : 2);
+        const int64_t r = mt * (9 * slots / nt);
+        if (r > lim) lim = r;
+    }
+    return lim;
+}
+
 // prefill_mt: the prefill tile rows to lay the work-lists out for; the small
 // tile (the default) yields the most items, so its layout bounds the others.
+// The fc2 partial sums and work-list are sized for the largest K split any
+// layer with at most R routes can take (S_max parts of up to
+// min(R, split_route_limit) routes), so the workspace never shrinks as T grows
+// and a workspace sized for the largest batch serves every smaller one.
 bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L,
                  int prefill_mt = qmoe::kPrefillMTSmall)
 {
@@ -171,14 +191,24 @@ bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L,
     const int fc2_cols = L->decode ? qmoe::kDecodeFc2Cols : qmoe::prefill_fc2_cols(L->m_tile);
     L->nt1 = (int)ceil_div(I, fc1_cols);
     L->nt2 = (int)ceil_div(H, fc2_cols);
-    const int64_t m_tiles = ceil_div(R, L->m_tile) + (E < R ? E : R);
+    auto tiles_of = [&](int64_t r) { return ceil_div(r, L->m_tile) + (E < r ? E : r); };
+    const int64_t m_tiles = tiles_of(R);
     L->m_tiles = m_tiles;
-    if (!mul_ok(m_tiles, L->nt1, &L->cap1) || !mul_ok(m_tiles, (int64_t)L->nt2 * L->k_split_cap, &L->cap2) ||
-        L->cap1 > INT32_MAX || L->cap2 > INT32_MAX) {
+    // y2 rows and fc2 work-list m-tiles, each the larger of the unsplit layer
+    // and the largest split one with at most R routes
+    int64_t y2_rows = R, wl2_tiles = m_tiles;
+    if (!L->decode) {
+        const int s_max = I % (4 * qmoe::kSuperK) == 0 ? 4 : I % (2 * qmoe::kSuperK) == 0 ? 2 : 1;
+        const int64_t r_split = R < split_route_limit(H) ? R : split_route_limit(H);
+        if (s_max * r_split > y2_rows) y2_rows = s_max * r_split;
+        if (s_max * tiles_of(r_split) > wl2_tiles) wl2_tiles = s_max * tiles_of(r_split);
+    }
+    if (!mul_ok(m_tiles, L->nt1, &L->cap1) || !mul_ok(wl2_tiles, L->nt2, &L->cap2) || L->cap1 > INT32_MAX ||
+        L->cap2 > INT32_MAX) {
         return false;
     }
     int64_t act_bytes, y2_bytes;
-    if (!mul_ok(R, (int64_t)I * 2, &act_bytes) || !mul_ok(R, (int64_t)H * 4 * L->k_split_cap, &y2_bytes)) {
+    if (!mul_ok(R, (int64_t)I * 2, &act_bytes) || !mul_ok(y2_rows, (int64_t)H * 4, &y2_bytes)) {
         return false;
     }
     // the projection kernels address hidden [T, H] and act [R, I] with 32-bit element offsets
@@ -210,6 +240,15 @@ bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L,
     L->n_counters = L->decode && blocks <= kMaxFusedCounters ? (int)blocks : 0;
     L->counters = take((size_t)L->n_counters * 4);
     L->total = off;
+    if (!L->decode) {
+        // at least the largest decode layout of the same layer (its m-tile
+        // list can outgrow the first prefill work-lists), so the size never
+        // drops where the decode path ends
+        Layout D;
+        if (make_layout(QMOE_DECODE_MAX_ROUTES / top_k, H, I, E, top_k, &D) && D.total > L->total) {
+            L->total = D.total;
+        }
+    }
     return true;
 }
 

@@ -265,11 +265,12 @@ def test_layer_decode_prefill_boundary(T, k):
     _layer_check(spec, 77 + T)
 
 
-@pytest.mark.parametrize("dtype,bits,zp,bs,act", [(2, (4, 4), "sym", 128, 0),
-                                                  (1, (4, 2), "u8", 64, 1),
+@pytest.mark.parametrize("dtype,bits,zp,bs,act", [(2, (4, 4), "sym", 32, 0),
+                                                  (1, (4, 2), "u8", 32, 1),
                                                   (2, (3, 2), "zpo", 32, 0)])
 def test_layer_large_prefill_tile(dtype, bits, zp, bs, act):
-    # 4096 routes against I = 8192: enough items for the 128-row prefill tile
+    # 4096 routes against I = 8192: enough items for the 128-row prefill tile,
+    # whose scale staging needs whole 8-block stages per row (H / 32 = 8)
     spec = synth.custom(T=2048, H=256, I=8192, E=4, k=2, fc1_bits=bits[0], fc2_bits=bits[1],
                         block_size=bs, dtype=dtype, act=act, zp_mode=zp,
                         zpo=1.5 if zp == "zpo" else math.nan, zp_range=(0, 3),
