@@ -237,43 +237,56 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
         auto compute = [&](const uint32_t* buf, const Span<BITS> (&cur)[4], const RawParams (&cbp)[4],
                            int s) {
             const int kk = s * kSuperK + 32 * g;
-            // the 64-row tile (one wavefront per SIMD when the grid is small)
-            // reads step t + 1's A fragments while step t computes
-            constexpr bool kAhead = MT == 64;
             auto frag = [&](int mb, int t) {
                 return *reinterpret_cast<const u32x4*>(buf + (mb * 16 + c) * kPitch + 16 * g + 4 * t);
             };
-            u32x4 next[kAhead ? MB : 1];
-            if constexpr (kAhead) {
+            auto dq = [&](int t, int nb) {
+                const RawParams rq = (TWO && t >= 2) ? params(nb, kk + 16) : cbp[nb];
+                const BlockParams q = decode_params<DT, BITS, ZP>(rq, p.w.zp_fallback);
+                return dequant_zp<DT, BITS, ZP>(cur[nb], t, q);
+            };
+            if constexpr (MT == kPrefillMTSmall) {
+                // The 64-row tile often runs one wavefront per SIMD, with no
+                // partner to fill its waits, so the step is software-pipelined
+                // by hand: fragment f = 4t + mb is read two fragments ahead of
+                // its MFMAs, and step t + 1's B registers are dequantized one
+                // column block per row block, between the MFMAs of step t.
+                // The scheduling barriers keep that order.
+                static_assert(MB == 4, "one column block dequantized per row block");
+                constexpr int kF = 4 * MB;
+                u32x4 ring[3];
+                ring[0] = frag(0, 0);
+                ring[1] = frag(1, 0);
+                u32x4 bf[4], bn[4];
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) next[mb] = frag(mb, 0);
-            }
+                for (int nb = 0; nb < 4; ++nb) bf[nb] = dq(0, nb);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                u32x4 held[kAhead ? MB : 1];
-                if constexpr (kAhead) {
+                for (int f = 0; f < kF; ++f) {
+                    const int t = f / MB, mb = f % MB;
+                    if (f + 2 < kF) ring[(f + 2) % 3] = frag((f + 2) % MB, (f + 2) / MB);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) held[mb] = next[mb];
-                    if (t + 1 < 4) {
+                    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = Dt<DT>::mfma(ring[f % 3], bf[nb], acc[mb][nb]);
+                    if (t + 1 < 4) bn[mb] = dq(t + 1, mb);  // MB == 4: one column block per row block
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (mb == MB - 1) {
 #pragma unroll
-                        for (int mb = 0; mb < MB; ++mb) next[mb] = frag(mb, t + 1);
+                        for (int nb = 0; nb < 4; ++nb) bf[nb] = bn[nb];
                     }
                 }
-                u32x4 bf[4];
+            } else {
+                // two wavefronts per SIMD: the compiler's own order, which
+                // measured faster here than the hand-pipelined one
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    const RawParams rq = (TWO && t >= 2) ? params(nb, kk + 16) : cbp[nb];
-                    const BlockParams q = decode_params<DT, BITS, ZP>(rq, p.w.zp_fallback);
-                    bf[nb] = dequant_zp<DT, BITS, ZP>(cur[nb], t, q);
-                }
+                for (int t = 0; t < 4; ++t) {
+                    u32x4 bf[4];
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    u32x4 af;
-                    if constexpr (kAhead) af = held[mb];
-                    else af = frag(mb, t);
+                    for (int nb = 0; nb < 4; ++nb) bf[nb] = dq(t, nb);
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) {
-                        acc[mb][nb] = Dt<DT>::mfma(af, bf[nb], acc[mb][nb]);
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const u32x4 af = frag(mb, t);
+#pragma unroll
+                        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = Dt<DT>::mfma(af, bf[nb], acc[mb][nb]);
                     }
                 }
             }
