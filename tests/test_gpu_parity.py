@@ -392,6 +392,25 @@ def test_layer_rows_decode(case):
     _layer_check(spec, 1400 + case)
 
 
+@pytest.mark.parametrize("T,k,path", [(6, 8, "decode"), (10, 8, "decode"), (200, 8, "prefill")])
+def test_layer_max_experts(T, k, path):
+    # E = 1024, the largest expert count: 16 experts per lane in the routing
+    # (decode plan and route kernel), the grouping's full expert table
+    spec = synth.custom(T=T, H=256, I=256, E=1024, k=k, fc1_bits=4, fc2_bits=2, block_size=32,
+                        dtype=2, act=0, zp_mode="sym", name=f"E1024_T{T}_{path}")
+    assert (T * k <= qm.DECODE_MAX_ROUTES) == (path == "decode")
+    _layer_check(spec, 1600 + T)
+
+
+def test_layer_top_k_64():
+    # one token over 64 experts of 256 (64 routes: the decode plan's ranks use
+    # both of its rank wavefronts' first lanes), and 20 tokens at top-32 (prefill)
+    _layer_check(synth.custom(T=1, H=256, I=256, E=256, k=64, fc1_bits=2, fc2_bits=4, block_size=32,
+                              dtype=1, act=1, zp_mode="sym", name="top64"), 1661)
+    _layer_check(synth.custom(T=20, H=256, I=256, E=64, k=32, fc1_bits=4, fc2_bits=4, block_size=64,
+                              dtype=2, act=0, zp_mode="sym", name="top32_prefill"), 1662)
+
+
 @pytest.mark.parametrize("T,E,k,fc1_bits", [(16, 4, 1, 3), (8, 70, 2, 4)])
 def test_layer_rows_decode_full_tile(T, E, k, fc1_bits):
     # every token's first choice is expert 1: one tile of T rows (16 and 8,
