@@ -47,18 +47,23 @@ constexpr int kXcds = 8;
 // eight blocks at a time (one 16-byte load per lane, a row per lane, issued a
 // stage ahead), and reads each super-step's scales from there; without it
 // every super-step loads them from HBM, 16 rows per instruction.
-template <int DT, int BITS, bool FC1, int MT, int ZP, bool TWO, bool STAGED>
-__global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
+// NBW: MFMA column blocks of 16 weight rows per wavefront: 4, or 2 (the
+// narrow 64-row tile: twice the items for layers with few of them, so more
+// wavefronts share each SIMD).
+template <int DT, int BITS, bool FC1, int MT, int ZP, bool TWO, bool STAGED, int NBW>
+__global__ __launch_bounds__(MT * 4, NBW == 4 ? 2 : 3) void prefill_kernel(ProjLaunch p)
 {
+    static_assert(NBW == 4 || (NBW == 2 && MT == kPrefillMTSmall), "the narrow tile is the 64-row one");
     constexpr Order O = code_order<DT, BITS>();
     constexpr int MB = MT / 16;
     constexpr int kThreads = MT * 4;        // 16 tile rows staged per wavefront
-    constexpr int kRows = MT * 4;           // weight rows per item (64 per wavefront)
+    constexpr int kWaveRows = 16 * NBW;     // weight rows per wavefront
+    constexpr int kRows = MB * kWaveRows;   // weight rows per item
     __shared__ __attribute__((aligned(16))) uint32_t a_lds[2][MT * kPitch];
     __shared__ int row_src[MT];  // A row of tile row i
     __shared__ int row_dst[MT];  // fc2: y2 row (route id) of tile row i
-    // STAGED: per wavefront, 64 row slots of 8 scales
-    __shared__ __attribute__((aligned(16))) uint16_t sc_lds[STAGED ? MT / 16 : 1][STAGED ? 64 * 8 : 1];
+    // STAGED: per wavefront, a row slot of 8 scales for each of its weight rows
+    __shared__ __attribute__((aligned(16))) uint16_t sc_lds[STAGED ? MB : 1][STAGED ? kWaveRows * 8 : 1];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -103,25 +108,27 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
         // reads the expert's first rows and stores nothing
         int col0;  // fc1: first activation column of this wave; fc2: first hidden column
         bool active;
-        uint32_t wrow[4];  // weight row within the expert's tensor of column block nb
+        uint32_t wrow[NBW];  // weight row within the expert's tensor of column block nb
         // fc1 column blocks 0 and 2 are gate rows of activation columns col0 + c
         // and col0 + 16 + c, blocks 1 and 3 their up rows, placed by the gate/up
-        // layout (interleaved, halves, or the separate fc3 tensor)
+        // layout (interleaved, halves, or the separate fc3 tensor); the narrow
+        // tile has blocks 0 and 1 only
         const int fusion = FC1 ? p.fusion : 1;
         const int I = p.N / 2;
         if constexpr (FC1) {
-            col0 = ntile * (kRows / 2) + wave * 32;
+            col0 = ntile * (kRows / 2) + wave * (kWaveRows / 2);
             active = col0 < I;
-            const int j0 = active ? col0 + c : 0, j1 = active ? col0 + 16 + c : 0;
-            wrow[0] = (uint32_t)fc1_row(fusion, j0, false, I);
-            wrow[1] = (uint32_t)fc1_row(fusion, j0, true, I);
-            wrow[2] = (uint32_t)fc1_row(fusion, j1, false, I);
-            wrow[3] = (uint32_t)fc1_row(fusion, j1, true, I);
+#pragma unroll
+            for (int h = 0; h < NBW / 2; ++h) {
+                const int j = active ? col0 + 16 * h + c : 0;
+                wrow[2 * h] = (uint32_t)fc1_row(fusion, j, false, I);
+                wrow[2 * h + 1] = (uint32_t)fc1_row(fusion, j, true, I);
+            }
         } else {
-            col0 = ntile * kRows + wave * 64;
+            col0 = ntile * kRows + wave * kWaveRows;
             active = col0 < p.N;
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) wrow[nb] = active ? col0 + nb * 16 + c : 0;
+            for (int nb = 0; nb < NBW; ++nb) wrow[nb] = active ? col0 + nb * 16 + c : 0;
         }
         // rows per expert of the (first) tensor: fc1 holds only the gate rows when fc3 holds the up rows
         const int64_t rows_e = (FC1 && fusion == 0) ? I : p.N;
@@ -133,27 +140,35 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
         const uint8_t* codes_u = sep ? p.w3.codes + erow * row_bytes : codes_e;
         const uint16_t* scales_u = sep ? reinterpret_cast<const uint16_t*>(p.w3.scales) + erow * n_blocks : scales_e;
         const uint8_t* zp_u = (ZP == kZpTensor && sep) ? p.w3.zp + erow * zp_bytes : zp_e;
-        const uint8_t* codes_nb[4] = {codes_e, codes_u, codes_e, codes_u};
-        const uint16_t* scales_nb[4] = {scales_e, scales_u, scales_e, scales_u};
-        const uint8_t* zp_nb[4] = {zp_e, zp_u, zp_e, zp_u};
+        const uint8_t* codes_nb[NBW];
+        const uint16_t* scales_nb[NBW];
+        const uint8_t* zp_nb[NBW];
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {  // odd blocks: the up rows
+            codes_nb[nb] = (nb & 1) ? codes_u : codes_e;
+            scales_nb[nb] = (nb & 1) ? scales_u : scales_e;
+            zp_nb[nb] = (nb & 1) ? zp_u : zp_e;
+        }
 
-        // STAGED: lane l loads the scales of one of the wavefront's 64 weight
-        // rows into slot l: fc2 rows col0 + l; fc1 with interleaved rows
-        // 2*col0 + l, slots interleaved so that the rows a load of column
-        // block nb reads sit in 16 consecutive slots (no LDS bank conflicts);
-        // fc1 with the other layouts the gate rows of columns col0 + l (l < 32)
-        // and the up rows of columns col0 + l - 32.
+        // STAGED: lane l loads the scales of one of the wavefront's weight
+        // rows (W = kWaveRows of them; the narrow tile's lanes W.. repeat lane
+        // l - W and store nothing) into slot l: fc2 rows col0 + l; fc1 with
+        // interleaved rows 2*col0 + l, slots interleaved so that the rows a
+        // load of column block nb reads sit in 16 consecutive slots (no LDS
+        // bank conflicts); fc1 with the other layouts the gate rows of columns
+        // col0 + l (l < W/2) and the up rows of columns col0 + l - W/2.
+        const int sl = lane & (kWaveRows - 1);
         const uint16_t* sc_row;
         int sc_slot_store;
         if (FC1 && fusion != 1) {
-            const int jl = active ? col0 + (lane & 31) : 0;
-            const bool up = lane >= 32;
+            const int jl = active ? col0 + (sl & (kWaveRows / 2 - 1)) : 0;
+            const bool up = sl >= kWaveRows / 2;
             sc_row = (up ? scales_u : scales_e) + fc1_row(fusion, jl, up, I) * n_blocks;
-            sc_slot_store = lane;
+            sc_slot_store = sl;
         } else {
             const uint32_t wr_base = active ? (FC1 ? 2 * col0 : col0) : 0;
-            sc_row = scales_e + (wr_base + lane) * n_blocks;
-            sc_slot_store = FC1 ? ((lane >> 1) | ((lane & 1) << 5)) : lane;
+            sc_row = scales_e + (wr_base + sl) * n_blocks;
+            sc_slot_store = FC1 ? ((sl >> 1) | ((sl & 1) * (kWaveRows / 2))) : sl;
         }
         const int stage_end = s_end >> ss_shift;  // parts hold whole stages
         u32x4 sc_next;
@@ -201,7 +216,8 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
             RawParams q;
             q.blk = kk >> bs_shift;
             if constexpr (STAGED) {
-                constexpr int kSlot[4] = {0, FC1 ? 32 : 16, FC1 ? 16 : 32, 48};
+                // slot of column block nb's row c (see the staging above)
+                constexpr int kSlot[4] = {0, FC1 ? kWaveRows / 2 : 16, FC1 ? 16 : 32, 48};
                 q.scale = sc_lds[wave][(c + kSlot[nb]) * 8 + (q.blk & 7)];
             } else {
                 q.scale = scales_nb[nb][wrow[nb] * n_blocks + q.blk];
@@ -212,29 +228,29 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
             }
             return q;
         };
-        auto load_b = [&](int s, Span<BITS> (&sp)[4], RawParams (&bp)[4]) {
+        auto load_b = [&](int s, Span<BITS> (&sp)[NBW], RawParams (&bp)[NBW]) {
             const int kk = s * kSuperK + 32 * g;
             if constexpr (STAGED) {
                 if ((s & ((1 << ss_shift) - 1)) == 0) {  // first super-step of a stage
-                    *reinterpret_cast<u32x4*>(&sc_lds[wave][sc_slot_store * 8]) = sc_next;
+                    if (lane < kWaveRows) *reinterpret_cast<u32x4*>(&sc_lds[wave][sc_slot_store * 8]) = sc_next;
                     const int next = (s >> ss_shift) + 1;
                     if (next < stage_end) stage_load(next);
                 }
             }
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
+            for (int nb = 0; nb < NBW; ++nb) {
                 sp[nb] = load_span<BITS>(codes_nb[nb] + wrow[nb] * row_bytes, kk);
                 bp[nb] = params(nb, kk);
             }
         };
 
-        f32x4 acc[MB][4];
+        f32x4 acc[MB][NBW];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        auto compute = [&](const uint32_t* buf, const Span<BITS> (&cur)[4], const RawParams (&cbp)[4],
+        auto compute = [&](const uint32_t* buf, const Span<BITS> (&cur)[NBW], const RawParams (&cbp)[NBW],
                            int s) {
             const int kk = s * kSuperK + 32 * g;
             auto frag = [&](int mb, int t) {
@@ -252,26 +268,26 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
                 // its MFMAs, and step t + 1's B registers are dequantized one
                 // column block per row block, between the MFMAs of step t.
                 // The scheduling barriers keep that order.
-                static_assert(MB == 4, "one column block dequantized per row block");
+                static_assert(MB == 4 && NBW <= MB, "at most one column block dequantized per row block");
                 constexpr int kF = 4 * MB;
                 u32x4 ring[3];
                 ring[0] = frag(0, 0);
                 ring[1] = frag(1, 0);
-                u32x4 bf[4], bn[4];
+                u32x4 bf[NBW], bn[NBW];
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) bf[nb] = dq(0, nb);
+                for (int nb = 0; nb < NBW; ++nb) bf[nb] = dq(0, nb);
 #pragma unroll
                 for (int f = 0; f < kF; ++f) {
                     const int t = f / MB, mb = f % MB;
                     if (f + 2 < kF) ring[(f + 2) % 3] = frag((f + 2) % MB, (f + 2) / MB);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = Dt<DT>::mfma(ring[f % 3], bf[nb], acc[mb][nb]);
-                    if (t + 1 < 4) bn[mb] = dq(t + 1, mb);  // MB == 4: one column block per row block
+                    for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = Dt<DT>::mfma(ring[f % 3], bf[nb], acc[mb][nb]);
+                    if (t + 1 < 4 && mb < NBW) bn[mb] = dq(t + 1, mb);
                     __builtin_amdgcn_sched_barrier(0);
                     if (mb == MB - 1) {
 #pragma unroll
-                        for (int nb = 0; nb < 4; ++nb) bf[nb] = bn[nb];
+                        for (int nb = 0; nb < NBW; ++nb) bf[nb] = bn[nb];
                     }
                 }
             } else {
@@ -279,31 +295,31 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
                 // measured faster here than the hand-pipelined one
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    u32x4 bf[4];
+                    u32x4 bf[NBW];
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) bf[nb] = dq(t, nb);
+                    for (int nb = 0; nb < NBW; ++nb) bf[nb] = dq(t, nb);
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) {
                         const u32x4 af = frag(mb, t);
 #pragma unroll
-                        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = Dt<DT>::mfma(af, bf[nb], acc[mb][nb]);
+                        for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = Dt<DT>::mfma(af, bf[nb], acc[mb][nb]);
                     }
                 }
             }
         };
 
-        Span<BITS> sp[4];
-        RawParams bp[4];
+        Span<BITS> sp[NBW];
+        RawParams bp[NBW];
         if constexpr (STAGED) stage_load(s_begin >> ss_shift);
         load_a(s_begin);
         load_b(s_begin, sp, bp);
         for (int s = s_begin; s < s_end; ++s) {
             uint32_t* buf = a_lds[s & 1];
             store_a(buf);
-            Span<BITS> cur[4];
-            RawParams cbp[4];
+            Span<BITS> cur[NBW];
+            RawParams cbp[NBW];
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
+            for (int nb = 0; nb < NBW; ++nb) {
                 cur[nb] = sp[nb];
                 cbp[nb] = bp[nb];
             }
@@ -323,11 +339,13 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
         // expert biases of this lane's four output columns [qmoe.rs,
         // qmoe_linear_impl: the bias entry of (expert, output row) is added to
         // the float32 projection output]; fc2 adds its bias in K part 0 only
-        float bias_v[4] = {0.f, 0.f, 0.f, 0.f};
+        float bias_v[NBW];
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) bias_v[nb] = 0.f;
         if constexpr (FC1) {
             const int js[2] = {col0 + c, col0 + 16 + c};
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < NBW / 2; ++h) {
                 if (p.bias) bias_v[2 * h] = p.bias[erow + fc1_row(fusion, js[h], false, I)];
                 if (sep) {
                     if (p.bias3) bias_v[2 * h + 1] = p.bias3[erow + js[h]];
@@ -337,7 +355,7 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
             }
         } else if (p.bias && ks == 0) {
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) bias_v[nb] = p.bias[erow + col0 + nb * 16 + c];
+            for (int nb = 0; nb < NBW; ++nb) bias_v[nb] = p.bias[erow + col0 + nb * 16 + c];
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -347,14 +365,15 @@ __global__ __launch_bounds__(MT * 4, 2) void prefill_kernel(ProjLaunch p)
                 if (m >= rows) continue;
                 if constexpr (FC1) {
                     uint16_t* out = reinterpret_cast<uint16_t*>(p.act_out) + (int64_t)(row0 + m) * I;
-                    out[col0 + c] = Dt<DT>::from_float(
-                        act_value<DT>(p.act, acc[mb][0][i] + bias_v[0], acc[mb][1][i] + bias_v[1], p.ap));
-                    out[col0 + 16 + c] = Dt<DT>::from_float(
-                        act_value<DT>(p.act, acc[mb][2][i] + bias_v[2], acc[mb][3][i] + bias_v[3], p.ap));
+#pragma unroll
+                    for (int h = 0; h < NBW / 2; ++h) {
+                        out[col0 + 16 * h + c] = Dt<DT>::from_float(act_value<DT>(
+                            p.act, acc[mb][2 * h][i] + bias_v[2 * h], acc[mb][2 * h + 1][i] + bias_v[2 * h + 1], p.ap));
+                    }
                 } else {
                     float* out = p.y2 + ks * p.part_stride + (int64_t)row_dst[m] * p.N;
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) out[col0 + nb * 16 + c] = acc[mb][nb][i] + bias_v[nb];
+                    for (int nb = 0; nb < NBW; ++nb) out[col0 + nb * 16 + c] = acc[mb][nb][i] + bias_v[nb];
                 }
             }
         }
@@ -406,16 +425,26 @@ hipError_t run(Kernel kernel, const ProjLaunch& p, int threads, hipStream_t s)
     return hipGetLastError();
 }
 
+template <bool FC1, int DT, int BITS, int MT, int ZP, int NBW>
+hipError_t launch_nbw(const ProjLaunch& p, hipStream_t s)
+{
+    if (can_stage(p, FC1)) return run(prefill_kernel<DT, BITS, FC1, MT, ZP, false, true, NBW>, p, MT * 4, s);
+    if constexpr (MT == kPrefillMTSmall) {
+        if (p.block_size < 32) return run(prefill_kernel<DT, BITS, FC1, MT, ZP, true, false, NBW>, p, MT * 4, s);
+        return run(prefill_kernel<DT, BITS, FC1, MT, ZP, false, false, NBW>, p, MT * 4, s);
+    }
+    return hipErrorInvalidValue;  // the large tile always stages its scales
+}
+
 template <bool FC1, int DT, int BITS, int MT, int ZP>
 hipError_t launch_one(const ProjLaunch& p, hipStream_t s)
 {
     if (!FC1 && (p.k_split < 1 || p.K % (p.k_split * kSuperK))) return hipErrorInvalidValue;
-    if (can_stage(p, FC1)) return run(prefill_kernel<DT, BITS, FC1, MT, ZP, false, true>, p, MT * 4, s);
     if constexpr (MT == kPrefillMTSmall) {
-        if (p.block_size < 32) return run(prefill_kernel<DT, BITS, FC1, MT, ZP, true, false>, p, MT * 4, s);
-        return run(prefill_kernel<DT, BITS, FC1, MT, ZP, false, false>, p, MT * 4, s);
+        if (p.nbw == 2) return launch_nbw<FC1, DT, BITS, MT, ZP, 2>(p, s);
     }
-    return hipErrorInvalidValue;  // the large tile always stages its scales
+    if (p.nbw != 4) return hipErrorInvalidValue;
+    return launch_nbw<FC1, DT, BITS, MT, ZP, 4>(p, s);
 }
 
 // The large tile serves the fast zero-point modes with stageable scales only

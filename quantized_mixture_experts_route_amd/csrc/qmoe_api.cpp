@@ -107,6 +107,7 @@ constexpr size_t kAlign = 256;
 struct Layout {
     bool decode;
     int m_tile;
+    int nbw;            // prefill: MFMA column blocks per wavefront (4, or 2: the narrow 64-row tile)
     int k_split_cap;    // prefill fc2: most K parts y2 and the fc2 work-list have room for
     int nt1, nt2;       // n-tiles of fc1 (activation columns) and fc2 (hidden columns)
     int64_t cap1, cap2;  // work-list capacities
@@ -131,12 +132,18 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // the target GPU; S = 2 or 4 is taken only when it cuts the estimated
 // makespan (in full-K item times) by more than a tenth.  The choice depends on
 // shapes only, so the workspace size does too.
-int fc2_split(int64_t R, int E, int H, int I, int mt)
+// Resident workgroups per CU of each prefill tile.
+int64_t tile_slots_per_cu(int mt, int nbw)
+{
+    return mt == qmoe::kPrefillMTLarge ? 1 : nbw == 2 ? 3 : 2;
+}
+
+int fc2_split(int64_t R, int E, int H, int I, int mt, int nbw = 4)
 {
     constexpr int64_t kCUs = 256;
-    const int64_t nt = ceil_div(H, qmoe::prefill_fc2_cols(mt));
+    const int64_t nt = ceil_div(H, qmoe::prefill_fc2_cols(mt, nbw));
     const int64_t items = (ceil_div(R, mt) + (E < R ? E : R) / 2) * nt;
-    const int64_t slots = kCUs * (mt == qmoe::kPrefillMTLarge ? 1 : 2);
+    const int64_t slots = kCUs * tile_slots_per_cu(mt, nbw);
     int best = 1;
     double best_cost = (double)ceil_div(items, slots);
     for (int S = 2; S <= 4; S *= 2) {
@@ -157,23 +164,25 @@ int fc2_split(int64_t R, int E, int H, int I, int mt)
 int64_t split_route_limit(int H)
 {
     int64_t lim = 0;
-    for (int mt : {qmoe::kPrefillMTSmall, qmoe::kPrefillMTLarge}) {
-        const int64_t nt = ceil_div(H, qmoe::prefill_fc2_cols(mt));
-        const int64_t slots = 256 * (mt == qmoe::kPrefillMTLarge ? 1 : 2);
-        const int64_t r = mt * (9 * slots / nt);
+    const int tiles[3][2] = {{qmoe::kPrefillMTSmall, 4}, {qmoe::kPrefillMTSmall, 2}, {qmoe::kPrefillMTLarge, 4}};
+    for (const auto& tl : tiles) {
+        const int64_t nt = ceil_div(H, qmoe::prefill_fc2_cols(tl[0], tl[1]));
+        const int64_t slots = 256 * tile_slots_per_cu(tl[0], tl[1]);
+        const int64_t r = tl[0] * (9 * slots / nt);
         if (r > lim) lim = r;
     }
     return lim;
 }
 
-// prefill_mt: the prefill tile rows to lay the work-lists out for; the small
-// tile (the default) yields the most items, so its layout bounds the others.
+// prefill_mt, nbw: the prefill tile to lay the work-lists out for; the narrow
+// small tile (the default) yields the most items, so its layout bounds the
+// others.
 // The fc2 partial sums and work-list are sized for the largest K split any
 // layer with at most R routes can take (S_max parts of up to
 // min(R, split_route_limit) routes), so the workspace never shrinks as T grows
 // and a workspace sized for the largest batch serves every smaller one.
 bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L,
-                 int prefill_mt = qmoe::kPrefillMTSmall)
+                 int prefill_mt = qmoe::kPrefillMTSmall, int nbw = 2)
 {
     int64_t R;
     if (T < 0 || H <= 0 || I <= 0 || E <= 0 || top_k <= 0 || !mul_ok(T, top_k, &R) ||
@@ -182,13 +191,16 @@ bool make_layout(int64_t T, int H, int I, int E, int top_k, Layout* L,
     }
     L->decode = R <= QMOE_DECODE_MAX_ROUTES;
     L->m_tile = L->decode ? qmoe::kDecodeMT : prefill_mt;
+    L->nbw = nbw;
     {
-        const int a = fc2_split(R, E, H, I, qmoe::kPrefillMTSmall);
+        const int a = fc2_split(R, E, H, I, qmoe::kPrefillMTSmall, 4);
+        const int a2 = fc2_split(R, E, H, I, qmoe::kPrefillMTSmall, 2);
         const int b = fc2_split(R, E, H, I, qmoe::kPrefillMTLarge);
-        L->k_split_cap = L->decode ? 1 : (a > b ? a : b);
+        const int ab = a > a2 ? a : a2;
+        L->k_split_cap = L->decode ? 1 : (ab > b ? ab : b);
     }
-    const int fc1_cols = L->decode ? qmoe::kDecodeFc1Cols : qmoe::prefill_fc1_cols(L->m_tile);
-    const int fc2_cols = L->decode ? qmoe::kDecodeFc2Cols : qmoe::prefill_fc2_cols(L->m_tile);
+    const int fc1_cols = L->decode ? qmoe::kDecodeFc1Cols : qmoe::prefill_fc1_cols(L->m_tile, nbw);
+    const int fc2_cols = L->decode ? qmoe::kDecodeFc2Cols : qmoe::prefill_fc2_cols(L->m_tile, nbw);
     L->nt1 = (int)ceil_div(I, fc1_cols);
     L->nt2 = (int)ceil_div(H, fc2_cols);
     auto tiles_of = [&](int64_t r) { return ceil_div(r, L->m_tile) + (E < r ? E : r); };
@@ -488,7 +500,14 @@ int qmoe_forward_ex(const void* hidden, const float* logits, int64_t T, int32_t 
                            aligned(w1.scales, 16) && aligned(w2.scales, 16);
     if (!L.decode && block_size >= 32 && w1.fast && w2.fast && stageable && !wide_codes &&
         (T * top_k / qmoe::kPrefillMTLarge) * ceil_div(I, qmoe::prefill_fc1_cols(qmoe::kPrefillMTLarge)) >= 1024) {
-        make_layout(T, H, I, E, top_k, &L, qmoe::kPrefillMTLarge);
+        make_layout(T, H, I, E, top_k, &L, qmoe::kPrefillMTLarge, 4);
+    } else if (!L.decode) {
+        // the 64-row tile: narrow (two column blocks per wavefront, twice the
+        // items) when its wide form leaves fewer than two fc1 items per CU
+        const int64_t R_ = T * top_k;
+        const int64_t items = (ceil_div(R_, qmoe::kPrefillMTSmall) + (E < R_ ? E : R_) / 2) *
+                              ceil_div(I, qmoe::prefill_fc1_cols(qmoe::kPrefillMTSmall, 4));
+        if (items >= 2 * 256) make_layout(T, H, I, E, top_k, &L, qmoe::kPrefillMTSmall, 4);
     }
     if (!hidden || !logits || !out) return fail(QMOE_ERR_INVALID_ARG, "hidden, logits and out must be non-NULL");
     if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(logits, 4)) {
@@ -508,7 +527,7 @@ int qmoe_forward_ex(const void* hidden, const float* logits, int64_t T, int32_t 
     // fc2 K parts: the shape policy's choice for this tile, halved until each
     // part holds whole super-steps and (for the large tile, which always
     // stages its scales) whole 8-block scale stages
-    int k_split = L.decode ? 1 : fc2_split(R, E, H, I, L.m_tile);
+    int k_split = L.decode ? 1 : fc2_split(R, E, H, I, L.m_tile, L.nbw);
     while (k_split > 1 && (I % (k_split * qmoe::kSuperK) ||
                            (L.m_tile == qmoe::kPrefillMTLarge && (I / k_split / block_size) % 8))) {
         k_split /= 2;
@@ -588,6 +607,7 @@ int qmoe_forward_ex(const void* hidden, const float* logits, int64_t T, int32_t 
     p1.block_size = block_size;
     p1.top_k = top_k;
     p1.m_tile = L.m_tile;
+    p1.nbw = L.nbw;
     p1.offsets = offsets;
     p1.sorted = sorted;
     p1.worklist = wl1;
@@ -617,6 +637,7 @@ int qmoe_forward_ex(const void* hidden, const float* logits, int64_t T, int32_t 
     p2.block_size = block_size;
     p2.top_k = top_k;
     p2.m_tile = L.m_tile;
+    p2.nbw = L.nbw;
     p2.offsets = offsets;
     p2.sorted = sorted;
     p2.worklist = wl2;

@@ -46,9 +46,10 @@ constexpr int kDecodeFc2Blocks = 2;  // 32 hidden columns
 constexpr int kSuperK = 128;  // inputs per K super-step: 4 lane groups x 32 codes
 
 // Output columns one work-list item covers (fc1 counts activation columns,
-// i.e. gate/up row pairs; fc2 counts hidden columns).
-constexpr int prefill_fc1_cols(int mt) { return 2 * mt; }
-constexpr int prefill_fc2_cols(int mt) { return 4 * mt; }
+// i.e. gate/up row pairs; fc2 counts hidden columns): mt/16 wavefronts of
+// nbw column blocks of 16 weight rows each.
+constexpr int prefill_fc1_cols(int mt, int nbw = 4) { return mt / 2 * nbw; }
+constexpr int prefill_fc2_cols(int mt, int nbw = 4) { return mt * nbw; }
 constexpr int kDecodeFc1Cols = kDecodeFc1Blocks * 16 / 2;
 constexpr int kDecodeFc2Cols = kDecodeFc2Blocks * 16;
 
@@ -99,6 +100,7 @@ struct ProjLaunch {
     int block_size;
     int top_k;
     int m_tile;               // prefill tile rows (kPrefillMTLarge or kPrefillMTSmall)
+    int nbw = 4;              // prefill: MFMA column blocks per wavefront (2: the narrow 64-row tile)
     const int32_t* offsets;   // [E+1]
     const int32_t* sorted;    // [R]
     const int32_t* worklist;  // prefill: [cap, 3] triples; decode: m-tiles
