@@ -1,5 +1,5 @@
 // gemm_stream.hip -- decode projections that stream every selected expert's
-// packed weights and consume them piece by piece as they land.
+// packed weights straight into the MFMA B registers.
 //
 // [PR 33569: the decode path serves small expanded-row counts, and its time
 // is set by the packed-weight bytes; qmoe.rs QMoEKernel::execute: route,
@@ -7,48 +7,52 @@
 // R = T*top_k <= 64 routes) every selected expert's weights are read once and
 // multiplied with at most 16 rows (a token routes to an expert at most once),
 // so a projection costs the time to stream its bytes plus the work left once
-// the last of them arrives.  One workgroup of eight wavefronts per
-// (expert, block of weight rows); wavefront w owns one block of 16 contiguous
-// weight rows and a 1/KS share of K.  fc1 (KS = 1): 128 rows per workgroup,
-// the 16 rows of a wavefront are 8 gate/up pairs, gate in MFMA columns 0-7
-// and up in 8-15, paired in the epilogue by a DPP rotate, so nothing is
-// reduced across wavefronts.  fc2 (KS = 2 when K allows): 64 rows per
-// workgroup and two wavefronts per block, whose partial sums meet once in LDS.
+// the last of them arrives.
 //
-// Order: fc1 loads the router logits of the wavefront's tokens, fc2 the
-// expert's offsets and route ids; then the scale table of the workgroup's
-// rows, one A row per wavefront (fc1 the tokens, all of them, since routing
-// is not known yet; fc2 the expert's rows) and the first two weight pieces of
-// the wavefront's block (one piece: one 128-byte line of each of its 16 rows,
-// eight whole lines per load instruction).  The workgroup's shared work
-// comes next: fc1 routes every token (the first workgroup writes the routing
-// weights, expert offsets and sorted routes for fc2 and the combine), and A,
-// its per-super-step corrections and the scales go to LDS.  Then each
-// wavefront requests the rest of its pieces and waits for no other wavefront
-// until fc2's two K shares meet at the end: requests are accepted only as
-// fast as earlier data returns, so a workgroup barrier after them would hold
-// every wavefront until the slowest had issued.  vmcnt retires loads in issue
-// order, so each wait names exactly its own loads (and an L2 hit issued after
-// the weight misses would wait for them: the small loads go first).  Piece j
-// is consumed as soon as it lands: copied to a wavefront-private LDS slot,
-// read back as MFMA spans, and multiplied with the A fragments of its
-// super-steps, whose MFMA chains are interleaved.  Scheduling barriers keep
-// the load groups in this order.
+// One workgroup of eight wavefronts per (expert, block of weight rows).  The
+// wavefronts split K: wavefront (rw, kw) owns S super-steps of 128 inputs
+// starting at kw * S * 128 (a K slice of 32, 64 or 128 bytes of every weight
+// row) for RBW blocks of 16 weight rows, so its A fragments (all 16 MFMA
+// rows of the slice: the tokens for fc1, the expert's routed rows for fc2)
+// fit in registers and are read from LDS once, not once per weight row block.
+// Every global request covers whole 64-byte segments:
+// - A: each wavefront copies its slice (rows past the last read as zeros
+//   through a bounds-checked buffer resource, without memory traffic) with
+//   contiguous 16-byte lanes into a wavefront-private LDS region and reads
+//   its fragments back;
+// - scales: the workgroup's rows are contiguous, so their scale rows form one
+//   block copied to an LDS table with 16-byte lanes;
+// - weights: lane 16g + c reads 16 contiguous bytes of weight row c (the
+//   four lanes of a row cover its 64-byte slice) and the lane groups trade
+//   8-byte pieces with v_permlane16_swap / v_permlane32_swap, so that lane
+//   group g holds the 32-code span MFMA lane group g consumes in each
+//   super-step (the same spans the prefill kernels read).
+// The only other LDS traffic is one float32 partial tile per wavefront and
+// row block (written over its own A region), summed over the K slices in
+// slice order (deterministic) by the epilogue.  Workgroup barriers wait for
+// LDS only (s_waitcnt lgkmcnt(0); s_barrier), never for the weight loads in
+// flight.
 //
-// MFMA mapping and dequantization are those of the other projection kernels:
-// lane 16g + c feeds A row c (a routed row; zeros past the expert's rows,
-// without reading LDS) and weight column c of the block, lane group g the inputs
-// [32g, 32g+32) of each 128-input super-step in the code order of the dequant
-// routines.  RAW (block_size a multiple of 128): the B registers are the raw
-// codes made exact dtype values by one v_and_or_b32 each, with a base b_r per
-// register r chosen so that the code's bits, where they already sit in the
-// packed word (or nearly), weigh 1 (fp16 int2: 1024, 256, 64, 16; int4: 1024
-// and 64), which saves most of the shifts that would bring every code down to
-// bit 0.  The zero point and the bases are taken out per
-// super-step in float32: sum_k (q_k - zp) a_k = mfma(a, b_r + q) -
-// sum_k (b_r(k) + zp) a_k, the last sum formed once per A row and super-step
-// while A is staged; the scale multiplies the difference.  Otherwise each
-// weight is dequantized in registers with a constant zero point.
+// Order of requests: fc1 the router logits and the A slice (the tokens),
+// fc2 the expert's offsets; the scales and the first half of the weight row
+// blocks; then fc1 routes every token (the first workgroup writes the routing
+// weights, expert offsets and sorted routes for fc2 and the combine) and a
+// workgroup whose expert has no rows leaves; fc2's A slice and the second
+// half of the weight blocks follow.  vmcnt retires loads in issue order, so
+// each wait names exactly the loads it needs, and the A slice is requested
+// before the weights it multiplies.  A slices cover AR = 8 or 16 rows (the
+// tokens or the expert's rows fit in 8 for T <= 8); MFMA rows past AR hold
+// whatever the LDS region held and are never stored.
+//
+// RAW (block_size a multiple of 128: one scale per lane and super-step): the
+// B registers are the raw codes made exact dtype values by one v_and_or_b32
+// each, with a base b_r per register r chosen so that the code's bits, where
+// they already sit in the packed word (or nearly), weigh 1.  The zero point
+// and the bases are taken out per super-step in float32:
+// sum_k (q_k - zp) a_k = mfma(a, b_r + q) - sum_k (b_r(k) + zp) a_k; the last
+// sum (the correction) starts the super-step's MFMA chain, and the scale
+// multiplies the chain's result.  Otherwise each weight is dequantized in
+// registers as (q - zp) * scale with a constant zero point.
 #include "gemm_common.h"
 #include "route_common.h"
 
@@ -57,18 +61,11 @@ namespace {
 
 constexpr int kWavesS = 8;
 constexpr int kThreadsS = kWavesS * kWave;
-constexpr int kRowsA = 16;                   // A tile rows: tokens (fc1) or expert rows (fc2)
+constexpr int kRowsA = 16;               // MFMA rows: tokens (fc1) or the expert's rows (fc2)
 constexpr int kMaxK = 2048;
-constexpr int kMaxSuper = kMaxK / kSuperK;
-constexpr int kPitchA = kMaxK / 2 + 4;       // A tile row pitch in 32-bit words (row r: bank 4r)
-constexpr int kLine = 128;                   // bytes of each weight row per piece
-constexpr int kSlotPitch = kLine + 16;       // LDS slot row pitch: 36 words, 16 rows on distinct banks
-constexpr int kMaxBlocks = 64;               // quantization blocks per row (K / block_size)
-constexpr int kScPitch = kMaxBlocks + 4;     // scale table row pitch in uint16 (rows 8-byte aligned)
-constexpr int kScUnits = 2;                  // 16-byte scale units per thread at most (128 rows x 8)
-constexpr int kTokW = kRowsA / kWavesS;      // tokens each wavefront routes (T <= 16)
-constexpr int kMaxRoutesS = kWave;           // routes (T * top_k), one per lane of wavefront 0
-constexpr int kDppRor8 = 0x128;              // DPP row_ror:8: lane c reads lane c ^ 8 of its row
+constexpr int kTokW = kRowsA / kWavesS;  // tokens each wavefront routes (T <= 16)
+constexpr int kGroupTok = 4;             // tokens per wavefront with 16 lanes per token (E <= 16)
+constexpr int kMaxRoutesS = kWave;       // routes (T * top_k), one per lane of wavefront 0
 
 // A kernel argument held in SGPRs from here on: the compiler may otherwise
 // fetch it again where it is used, and a fetch issued after the weight
@@ -80,165 +77,95 @@ __device__ inline T held(T v)
     return v;
 }
 
-// The piece loop of the streamed projections.  Piece j of bv (load i: rows
-// 8i + lane/8 of the 16-row block, 16 bytes at 16*(lane%8) of the piece)
-// lands in the wavefront's LDS slot, row r at slot row slot_of(r); then its
-// SPP super-steps run as independent MFMA chains.  a_row: this lane's A row
-// (row_ok: a real one); sc_row: the scale table row of MFMA column c;
-// corr(S): the RAW corrections of MFMA rows 4g..4g+3 at super-step S (s0 +
-// local index).  Lanes past the real rows keep stale A fragments, which reach
-// only MFMA rows that are never stored; a skipped super-step (past the K
-// share) keeps them too and is cancelled by a zero scale.  Returns the sum of
-// the chains.
-template <int DT, int BITS, int P, bool RAW, class SlotOf, class Corr>
-__device__ inline f32x4 consume_pieces(const u32x4 (&bv)[P][2], uint8_t* slot, SlotOf slot_of,
-                                       const uint32_t* a_row, bool row_ok, const uint16_t* sc_row,
-                                       Corr corr, int s0, int n_super, int bs_shift, float zp,
-                                       const uint32_t (&magic)[4])
+// Buffer resource over `bytes` bytes from `base`: a load at an offset past the
+// end returns zeros and touches no memory.
+__device__ inline __amdgpu_buffer_rsrc_t bounded(const void* base, uint32_t bytes)
 {
-    constexpr int SPP = kLine * 8 / BITS / kSuperK;
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 4;
-    const int c = lane & 15;
-    const int lrow = lane >> 3;
-    const int lbyte = 16 * (lane & 7);
-    f32x4 acc[SPP];
-#pragma unroll
-    for (int sp = 0; sp < SPP; ++sp) acc[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 a4[SPP][4];
-#pragma unroll
-    for (int sp = 0; sp < SPP; ++sp)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) a4[sp][t] = u32x4{0u, 0u, 0u, 0u};
-
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-        if (j * SPP >= n_super) break;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            *reinterpret_cast<u32x4*>(slot + slot_of(8 * i + lrow) * kSlotPitch + lbyte) = bv[j][i];
-        }
-        // gather the piece: A fragments, spans, corrections and scales
-        Span<BITS> spn[SPP];
-        f32x4 rs[SPP];
-        float scl[SPP];
-#pragma unroll
-        for (int sp = 0; sp < SPP; ++sp) {
-            const int s = j * SPP + sp;
-            const bool ok = s < n_super;  // uniform
-            const int S = s0 + min(s, n_super - 1);  // the super-step in K
-            if (ok && row_ok) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    a4[sp][t] = *reinterpret_cast<const u32x4*>(a_row + (S * kSuperK + 32 * g) / 2 + 4 * t);
-                }
-            }
-            spn[sp] = load_span<BITS>(slot + c * kSlotPitch, sp * kSuperK + 32 * g);
-            const float sv = Dt<DT>::to_float(sc_row[(S * kSuperK + (RAW ? 0 : 32 * g)) >> bs_shift]);
-            scl[sp] = ok ? sv : 0.f;
-            if constexpr (RAW) rs[sp] = corr(S);
-        }
-        if constexpr (RAW) {
-            f32x4 part[SPP];
-#pragma unroll
-            for (int sp = 0; sp < SPP; ++sp) part[sp] = rs[sp];
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int sp = 0; sp < SPP; ++sp)
-                    part[sp] = Dt<DT>::mfma(a4[sp][t], raw_step_based<DT, BITS>(spn[sp], t, magic), part[sp]);
-#pragma unroll
-            for (int sp = 0; sp < SPP; ++sp) acc[sp] += part[sp] * scl[sp];
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int sp = 0; sp < SPP; ++sp) {
-                    BlockParams bq;
-                    bq.zp = zp;
-                    bq.scale = scl[sp];
-                    acc[sp] = Dt<DT>::mfma(a4[sp][t], dequant_zp<DT, BITS, kZpConst>(spn[sp], t, bq), acc[sp]);
-                }
-        }
-    }
-    f32x4 sum = acc[0];
-#pragma unroll
-    for (int sp = 1; sp < SPP; ++sp) sum += acc[sp];
-    return sum;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// The A staging of the streamed projections: one A row of 16-byte chunks
-// (chunk lane + 64*qq), permuted to the MFMA register order (int2 pairs the
-// chunks of lanes l and l^1, both in the same row) into LDS row `dst`, and
-// for RAW the row's per-super-step corrections -sum (b_r + zp) a (16 lanes
-// hold one super-step) stored through put(super-step, value).
-template <int DT, int BITS, bool RAW, class Put>
-__device__ inline void stage_a_row(const u32x4 (&av)[4], bool valid, int cpr, uint32_t* dst, float zp, Put put)
+// The dtype's (1, 1) pair, the B operand of a plain sum in v_dot2.
+template <int DT>
+__device__ inline float dot2_sum(uint32_t a, float acc)
 {
+    if constexpr (DT == kF16) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, ones2<DT>()), acc, false);
+    } else {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, ones2<DT>()), acc,
+                                               false);
+    }
+}
+
+// Workgroup barrier for LDS data only: loads from global memory stay in flight.
+__device__ inline void sync_lds()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// The 64-byte K slice of a weight row read by lane group g as bytes
+// [16g, 16g+16) (8-byte pieces 2g and 2g+1) becomes pieces g and g + 4 of
+// lane group g, super-steps 0 and 1 of its span: a transpose of 16-lane
+// blocks by v_permlane16_swap (odd rows of the first operand with even rows
+// of the second), then v_permlane32_swap (upper half of the first with lower
+// half of the second).
+__device__ inline void spans_of_slice(const u32x4& v, Span<2>& s0, Span<2>& s1)
+{
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        const auto a = __builtin_amdgcn_permlane16_swap(v[d], v[d + 2], false, false);
+        const auto b = __builtin_amdgcn_permlane32_swap(a[0], a[1], false, false);
+        s0.w[d] = b[0];
+        s1.w[d] = b[1];
+    }
+}
+
+template <int DT, int BITS, bool FC1, int S, int KSW, int RBW, int AR, bool GR, bool RAW>
+__global__ __launch_bounds__(kThreadsS, RBW <= 4 ? 4 : 2) void stream_kernel(ProjLaunch p, DecodePlan q)
+{
+    constexpr int RW = kWavesS / KSW;              // wavefronts along the rows
+    constexpr int kBlocksWG = RW * RBW;            // 16-row weight blocks per workgroup
+    constexpr int kRowsWG = 16 * kBlocksWG;
+    constexpr int kEarly = (RBW + 1) / 2;          // row blocks requested before the rows are known
+    constexpr int kSliceK = S * kSuperK;           // inputs of a K slice
+    constexpr int kSliceB = kSliceK * BITS / 8;    // bytes of a weight row in a K slice: 32, 64 or 128
+    constexpr int kAPitch = kSliceK / 2 + 4;       // A region row pitch in words (row r: bank 4r)
+    constexpr int kAWords = kRowsA * kAPitch;      // A region of a wavefront
+    constexpr int kARowsPerLoad = 512 / kSliceK;   // A rows one load instruction covers
+    constexpr int kALoads = AR / kARowsPerLoad;    // 16-byte A loads per lane: AR rows (8 or 16)
+    constexpr int kScBlocks = RAW ? kMaxK / kSuperK : kMaxK / 32;  // scale blocks per row at most
+    constexpr int kScPitch = kScBlocks + 2;        // scale table row pitch in uint16 (odd word count)
+    constexpr int kScUnits = (kRowsWG * kScBlocks / 8 + kThreadsS - 1) / kThreadsS;  // 16-byte units per thread
     constexpr Order O = RAW ? raw_order<BITS>() : code_order<DT, BITS>();
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-        const int ch = lane + kWave * qq;
-        u32x4 v;
-        if constexpr (O == Order::kStride8) v = permute_chunk_pair(av[qq], lane & 1);
-        else v = permute_chunk<O>(av[qq]);
-        if constexpr (RAW) {
-            float part = 0.f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float coef = -(raw_base<DT, BITS>(r) + zp);
-                part += coef * Dt<DT>::to_float((uint16_t)(v[r] & 0xffffu));
-                part += coef * Dt<DT>::to_float((uint16_t)(v[r] >> 16));
-            }
-            part += dpp_f32<kDppXor1>(part);
-            part += dpp_f32<kDppXor2>(part);
-            part += dpp_f32<kDppHalfMirror>(part);
-            part += dpp_f32<kDppMirror>(part);
-            if (valid && ch < cpr && (lane & 15) == 0) put(ch >> 4, part);
-        }
-        if (valid && ch < cpr) *reinterpret_cast<u32x4*>(dst + 4 * ch) = v;
-    }
-}
-
-template <int DT, int BITS, bool FC1, int KS, int P, bool RAW>
-__global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, DecodePlan q)
-{
-    constexpr int kBlocksWG = kWavesS / KS;             // 16-row weight blocks per workgroup
-    constexpr int kRowsWG = 16 * kBlocksWG;             // weight rows per workgroup
-    constexpr int kEarly = P < 2 ? P : 2;               // pieces requested before the shared work
-    static_assert(BITS == 2 || BITS == 4, "a 128-byte line holds whole super-steps");
-    static_assert(!FC1 || KS == 1, "fc1 pairs gate and up columns within one wavefront");
-    __shared__ __attribute__((aligned(16))) uint32_t a_tile[kRowsA * kPitchA];
-    __shared__ __attribute__((aligned(16))) uint8_t b_slot[kWavesS][16 * kSlotPitch];
+    static_assert(BITS == 2 || BITS == 4, "spans of whole 32-bit words");
+    static_assert(kSliceB == 32 || kSliceB == 64 || kSliceB == 128, "K slice of a weight row");
+    static_assert(RBW * 256 <= kAWords, "partial tiles fit the wavefront's A region");
+    // per wavefront: its A slice [16][kAPitch] words, later its partial
+    // tiles [RBW][16 MFMA rows][16 columns] float32
+    __shared__ __attribute__((aligned(16))) uint32_t a_reg[kWavesS][kAWords];
     __shared__ __attribute__((aligned(16))) uint16_t sc_tab[kRowsWG * kScPitch];
-    __shared__ float a_sum[kRowsA][kMaxSuper];  // RAW: -sum (b_r + zp) a of A row m over super-step s
-    __shared__ __attribute__((aligned(16))) float m_sum[kMaxSuper][kRowsA];  // RAW: the same by MFMA row
-    __shared__ __attribute__((aligned(16))) float red[KS == 2 ? kBlocksWG * kWave * 4 : 4];
     __shared__ int s_e[kMaxRoutesS];  // fc1: expert of route r
-    __shared__ int s_arow[kRowsA];  // fc1: A tile row (token) of the expert's m-th route
-    __shared__ int s_info[2];       // fc1: first sorted position, route count
+    __shared__ int s_route[kRowsA];   // fc2: route id of the expert's row m
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int g = lane >> 4;
     const int c = lane & 15;
-    const int rb = wave % kBlocksWG;  // the wavefront's weight row block
-    const int kp = wave / kBlocksWG;  // its share of K
+    const int kw = wave % KSW;  // the wavefront's K slice
+    const int rw = wave / KSW;  // its row blocks
     const int K = p.K;
-    const int KW = K / KS;            // inputs per wavefront
-    const int s0 = kp * (KW / kSuperK);  // its first super-step
-    const int n_super = KW / kSuperK;
-    const int n_blocks = K / p.block_size;
+    const int k0 = kw * kSliceK;  // first input of the slice
     const int bs_shift = __builtin_ctz((unsigned)p.block_size);  // a power of two
+    const int n_blocks = K >> bs_shift;
     const int nt = p.N / kRowsWG;
     const int e = blockIdx.x / nt;
     const int n = blockIdx.x - e * nt;
     const int row_bytes = K * BITS / 8;
-    const int wr0 = n * kRowsWG + 16 * rb;  // first weight row of the block within the expert
-    const int col0 = FC1 ? wr0 / 2 : wr0;   // first output column (fc1: 8 activation columns)
-    const uint16_t* a_src = reinterpret_cast<const uint16_t*>(p.a);
+    const int wr0 = n * kRowsWG + 16 * RBW * rw;  // first weight row of the wavefront within the expert
     uint32_t magic[4];  // RAW: per-register bases
 #pragma unroll
     for (int r = 0; r < 4; ++r) magic[r] = opaque(raw_magic<DT, BITS>(r));
@@ -246,253 +173,370 @@ __global__ __launch_bounds__(kThreadsS, 1) void stream_kernel(ProjLaunch p, Deco
     const int act = held(p.act);
     uint16_t* const act_out = held(reinterpret_cast<uint16_t*>(p.act_out));
     float* const y2 = held(p.y2);
+    uint32_t* const a_mine = a_reg[wave];
 
     // Every load below is issued unconditionally (indices clamped): a load
     // under a branch leaves its register undefined on the other path, and the
     // compiler then waits for it on the spot.
-    // 0) fc1: router logits of tokens wave and wave + 8; fc2: the expert's
-    //    rows in the sorted order (written by fc1) and their route ids
-    float lg[kTokW];
+    // 0) fc1: router logits (GR: lane 16i + j holds expert j of token
+    //    4 wave + i; otherwise tokens wave and wave + 8, expert lane);
+    //    fc2: the expert's offsets
+    constexpr int kLg = GR ? 1 : kTokW;
+    float lg[kLg];
     int first = 0, count = 0;
-    int y2_row[4] = {0, 0, 0, 0};  // fc2: route ids of rows 4g..4g+3 (clamped)
     if constexpr (FC1) {
 #pragma unroll
-        for (int j = 0; j < kTokW; ++j) {
-            const int t = min(wave + kWavesS * j, q.T - 1);
-            lg[j] = q.logits[(int64_t)t * q.E + min(lane, q.E - 1)];
+        for (int j = 0; j < kLg; ++j) {
+            const int t = min(GR ? kGroupTok * wave + (lane >> 4) : wave + kWavesS * j, q.T - 1);
+            lg[j] = q.logits[(int64_t)t * q.E + min(GR ? (lane & 15) : lane, q.E - 1)];
         }
     } else {
         first = q.offsets[e];
         count = q.offsets[e + 1] - first;
-        if (count == 0) {  // no rows of this expert: arrive on the column block only
-            if (p.fused.counters) fc2_arrive_combine<DT>(p.fused, y2, p.N, p.top_k, n, n * kRowsWG, kRowsWG, q.E);
-            return;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) y2_row[i] = q.sorted[first + min(4 * g + i, count - 1)];
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 1) scale table: 16-byte units of 8 blocks, row-major over the workgroup's rows
+    // The A slice: load i of a lane reads row kARowsPerLoad * i + lane / (64 /
+    // kARowsPerLoad), 16 contiguous bytes; rows past the last read zeros
+    u32x4 araw[kALoads];
+    auto load_a = [&](const void* base, int rows) {
+        const __amdgpu_buffer_rsrc_t rs = bounded(base, (uint32_t)rows * (uint32_t)K * 2u);
+        constexpr int kLanesPerRow = 64 / kARowsPerLoad;
+        const int r_in = lane / kLanesPerRow, ch = lane % kLanesPerRow;
+#pragma unroll
+        for (int i = 0; i < kALoads; ++i) {
+            const int r = kARowsPerLoad * i + r_in;
+            const uint32_t off = r < rows ? (uint32_t)(r * K + k0 + 8 * ch) * 2u : 0x80000000u;
+            araw[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        }
+    };
+    auto store_a = [&]() {
+        constexpr int kLanesPerRow = 64 / kARowsPerLoad;
+        const int r_in = lane / kLanesPerRow, ch = lane % kLanesPerRow;
+#pragma unroll
+        for (int i = 0; i < kALoads; ++i)
+            *reinterpret_cast<u32x4*>(a_mine + (kARowsPerLoad * i + r_in) * kAPitch + 4 * ch) = araw[i];
+    };
+    // 1) fc1: the A slice (the tokens, known before routing)
+    if constexpr (FC1) load_a(p.a, q.T);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2) the scale rows of the workgroup's weight rows: one contiguous block
+    //    of kRowsWG * n_blocks values, 16-byte units of 8 blocks
     const uint16_t* sc_src =
         reinterpret_cast<const uint16_t*>(p.w.scales) + ((int64_t)e * p.N + n * kRowsWG) * n_blocks;
-    const int upr = n_blocks >> 3;  // units per row
+    const int upr = n_blocks >> 3;  // units per row (n_blocks is a multiple of 8)
     const int n_units = kRowsWG * upr;
     u32x4 sc_unit[kScUnits];
 #pragma unroll
     for (int k = 0; k < kScUnits; ++k) {
         const int u = min(tid + kThreadsS * k, n_units - 1);
-        const int r = u / upr;
-        sc_unit[k] = *reinterpret_cast<const u32x4*>(sc_src + r * n_blocks + 8 * (u - r * upr));
+        sc_unit[k] = *reinterpret_cast<const u32x4*>(sc_src + 8 * u);
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2) A row `wave` (rows 8.. are loaded when staged): 16-byte chunk
-    //    lane + 64*qq, so each load reads whole lines
-    const int a_rows = FC1 ? q.T : count;
-    const int cpr = K / 8;  // 16-byte chunks per A row (a multiple of 16)
-    u32x4 av[4];
-    auto load_a = [&](int m) {
-        const uint16_t* row = a_src + (int64_t)(FC1 ? min(m, a_rows - 1) : first + min(m, a_rows - 1)) * K;
+    // weight row block rb: lane (g, c) reads bytes [16g, 16g+16) of row
+    // wr0 + 16 rb + c's slice (and [64+16g, ...) for a 128-byte slice; a
+    // 32-byte slice: bytes [8g, 8g+8), the span itself)
+    constexpr int kWLoads = kSliceB == 128 ? 2 : 1;
+    typedef typename std::conditional<kSliceB == 32, uint2, u32x4>::type WLoad;
+    WLoad wraw[RBW][kWLoads];
+    const uint8_t* w_row = p.w.codes + ((int64_t)e * p.N + wr0 + c) * row_bytes + (k0 * BITS / 8);
+    auto load_w = [&](int rb) {
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            av[qq] = *reinterpret_cast<const u32x4*>(row + 8 * min(lane + kWave * qq, cpr - 1));
-        }
+        for (int i = 0; i < kWLoads; ++i)
+            wraw[rb][i] = *reinterpret_cast<const WLoad*>(w_row + rb * 16 * row_bytes + 64 * i +
+                                                          (kSliceB == 32 ? 8 : 16) * g);
     };
-    load_a(wave);
+
+#pragma unroll
+    for (int rb = 0; rb < kEarly; ++rb) load_w(rb);
     __builtin_amdgcn_sched_barrier(0);
 
-    // 3) the first kEarly weight pieces of the wavefront: piece j, load i
-    //    reads rows 8i + lane/8 of the block, bytes [128j + 16*(lane%8), +16)
-    //    of its K share (clamped into the share past its end; those
-    //    super-steps are skipped).  The rest follow once the workgroup's
-    //    shared work is done.
-    const int kb0 = s0 * kSuperK * BITS / 8;  // first byte of the share in a row
-    const int kbw = KW * BITS / 8;            // bytes of the share
-    const uint8_t* wcodes = p.w.codes + ((int64_t)e * p.N + wr0) * row_bytes + kb0;
-    const int lrow = lane >> 3;
-    const int lbyte = 16 * (lane & 7);
-    u32x4 bv[P][2];
-    auto load_piece = [&](int j) {
+    auto store_scales = [&]() {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int ob = min(kLine * j + lbyte, kbw - 16);
-            bv[j][i] = *reinterpret_cast<const u32x4*>(wcodes + (8 * i + lrow) * row_bytes + ob);
+        for (int k = 0; k < kScUnits; ++k) {
+            const int u = tid + kThreadsS * k;
+            if (u < n_units) {
+                const int r = u / upr;
+                uint32_t* dst = reinterpret_cast<uint32_t*>(sc_tab + r * kScPitch + 8 * (u - r * upr));
+                dst[0] = sc_unit[k].x;
+                dst[1] = sc_unit[k].y;
+                dst[2] = sc_unit[k].z;
+                dst[3] = sc_unit[k].w;
+            }
         }
     };
-#pragma unroll
-    for (int j = 0; j < kEarly; ++j) load_piece(j);
-    __builtin_amdgcn_sched_barrier(0);
 
-    // 4) fc1: route every token; this expert's routes in ascending order,
-    //    and their first sorted position
+    // 3) fc1: route every token (GR: four tokens per wavefront, so the first
+    //    T / 4 wavefronts route; otherwise one wavefront per token); the
+    //    other wavefronts go on to their A fragments
     if constexpr (FC1) {
-        const int R = q.T * p.top_k;
         const bool writer = blockIdx.x == 0;
         // the fc2 launch's column-block counters start at zero
         if (writer && tid < q.n_counters) {
             __hip_atomic_store(&q.counters[tid], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-#pragma unroll
-        for (int j = 0; j < kTokW; ++j) {
-            const int t = wave + kWavesS * j;
-            if (t >= q.T) break;
-            route_values<1>(q.E, p.top_k, q.normalize, [&](int) { return lg[j]; },
-                            [&](int slot, int ex, float w) {
-                                const int r = t * p.top_k + slot;
-                                s_e[r] = ex;
-                                if (writer) {
-                                    q.weights[r] = w;
-                                    if (q.ids_out) q.ids_out[r] = ex;
-                                    if (q.w_out) q.w_out[r] = w;
-                                }
-                            });
-        }
-        __syncthreads();
-        if (wave == 0) {
-            const int ex = lane < R ? s_e[lane] : -1;
-            const uint64_t mine = __ballot(ex == e);
-            const uint64_t below = __ballot(lane < R && ex < e);
-            if (ex == e) s_arow[__popcll(mine & ((1ull << lane) - 1ull))] = lane / p.top_k;
-            if (lane == 0) {
-                s_info[0] = __popcll(below);
-                s_info[1] = __popcll(mine);
-            }
-            if (writer) {  // offsets and sorted routes of every expert, for fc2 and the combine
-                if (lane < R) {
-                    int less = 0, same_before = 0;
-                    for (int r = 0; r < R; ++r) {
-                        const int o = s_e[r];
-                        less += o < ex;
-                        same_before += (o == ex) & (r < lane);
-                    }
-                    q.sorted[less + same_before] = lane;
+        auto emit_for = [&](int t) {
+            return [&, t](int slot, int ex, float w) {
+                if (t >= q.T) return;
+                const int r = t * p.top_k + slot;
+                s_e[r] = ex;
+                if (writer) {
+                    q.weights[r] = w;
+                    if (q.ids_out) q.ids_out[r] = ex;
+                    if (q.w_out) q.w_out[r] = w;
                 }
-                // no loop around the stores: the compiler would drain every
-                // load in flight before entering it
-                if (lane < q.E) {
-                    int less = 0;
-                    for (int r = 0; r < R; ++r) less += s_e[r] < lane;
-                    q.offsets[lane] = less;
-                }
-                if (lane == 0) q.offsets[q.E] = R;
-            }
-        }
-        __syncthreads();
-        first = s_info[0];
-        count = s_info[1];
-        if (count == 0) return;  // whole workgroup; its first pieces drain on their own
-    }
-
-    // 5) A tile (permuted to the MFMA register order; int2 pairs the chunks of
-    //    lanes l and l^1, both in the same row), the row sums of its
-    //    super-steps (RAW) and the scale table to LDS
-    auto store_a = [&](int m) {
-        stage_a_row<DT, BITS, RAW>(av, m < a_rows, cpr, a_tile + m * kPitchA, zp,
-                                   [&](int sstep, float v) { a_sum[m][sstep] = v; });
-    };
-    store_a(wave);
-    if (a_rows > kWavesS) {  // rows 8..15
-        load_a(wave + kWavesS);
-        store_a(wave + kWavesS);
-    }
-#pragma unroll
-    for (int k = 0; k < kScUnits; ++k) {
-        const int u = tid + kThreadsS * k;
-        if (u < n_units) {
-            const int r = u / upr;
-            uint32_t* dst = reinterpret_cast<uint32_t*>(sc_tab + r * kScPitch + 8 * (u - r * upr));
-            *reinterpret_cast<u32x2*>(dst) = u32x2{sc_unit[k].x, sc_unit[k].y};
-            *reinterpret_cast<u32x2*>(dst + 2) = u32x2{sc_unit[k].z, sc_unit[k].w};
-        }
-    }
-    __syncthreads();
-    const bool row_ok = c < count;
-    const int arow = row_ok ? (FC1 ? s_arow[c] : c) : 0;
-    if constexpr (RAW) {  // corrections by MFMA row: m_sum[s][m] = a_sum[A row of route m][s]
-        if (tid < kMaxSuper * kRowsA) {
-            const int s = tid >> 4, m = tid & 15;
-            m_sum[s][m] = m < count ? a_sum[FC1 ? s_arow[m] : m][s] : 0.f;
-        }
-        __syncthreads();
-    }
-
-    // 6) the rest of the wavefront's weight pieces
-#pragma unroll
-    for (int j = kEarly; j < P; ++j) load_piece(j);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // 7) the pieces, each as soon as it lands
-    const uint32_t* a_row = a_tile + arow * kPitchA;
-    // MFMA column c of the block: fc1 gate row 2c (c < 8) or up row 2(c-8)+1,
-    // stored in slot c; fc2 row c
-    const int wrow = FC1 ? 2 * (c & 7) + (c >> 3) : c;
-    const uint16_t* sc_row = sc_tab + (16 * rb + wrow) * kScPitch;
-    uint8_t* slot = b_slot[wave];
-
-    f32x4 sum = consume_pieces<DT, BITS, P, RAW>(
-        bv, slot, [&](int row) { return FC1 ? (row >> 1) + 8 * (row & 1) : row; }, a_row, row_ok, sc_row,
-        [&](int S) { return *reinterpret_cast<const f32x4*>(&m_sum[S][4 * g]); }, s0, n_super, bs_shift, zp,
-        magic);
-
-    // 8) epilogue: lane (g, c) holds MFMA rows 4g..4g+3 of column c
-    bool stores = true;
-    if constexpr (KS == 2) {  // the second K share hands its sums to the first
-        f32x4* r4 = reinterpret_cast<f32x4*>(red) + rb * kWave + lane;
-        if (kp == 1) *r4 = sum;
-        __syncthreads();
-        stores = kp == 0;
-        if (stores) sum += *r4;
-    }
-#pragma unroll
-    for (int i = 0; i < 4 && stores; ++i) {
-        const int m = 4 * g + i;
-        if constexpr (FC1) {
-            const float up = dpp_f32<kDppRor8>(sum[i]);  // column c + 8: the up row of column c
-            if (m < count && c < 8) {
-                const int I = p.N / 2;
-                uint16_t* out = act_out + (int64_t)(first + m) * I;
-                out[col0 + c] = Dt<DT>::from_float(act_value<DT>(act, sum[i], up, p.ap));
+            };
+        };
+        if constexpr (GR) {
+            if (kGroupTok * wave < q.T) {
+                route_group<16>(q.E, p.top_k, q.normalize, lg[0], emit_for(kGroupTok * wave + (lane >> 4)));
             }
         } else {
-            if (m < count) store_y2(&y2[(int64_t)y2_row[i] * p.N + col0 + c], sum[i], p.fused.counters != nullptr);
+#pragma unroll
+            for (int j = 0; j < kTokW; ++j) {
+                const int t = wave + kWavesS * j;
+                if (t >= q.T) break;
+                route_values<1>(q.E, p.top_k, q.normalize, [&](int) { return lg[j]; }, emit_for(t));
+            }
+        }
+    } else {
+        if (count == 0) {  // no rows of this expert: arrive on the column block only
+            if (p.fused.counters) fc2_arrive_combine<DT>(p.fused, y2, p.N, p.top_k, n, n * kRowsWG, kRowsWG, q.E);
+            return;
         }
     }
+
+    // 4) fc2: the expert's route ids and rows (sorted activations); both: the
+    //    rest of the weight row blocks, then the scale table (its barrier waits
+    //    for LDS only)
+    int my_route = 0;
     if constexpr (!FC1) {
-        if (p.fused.counters) fc2_arrive_combine<DT>(p.fused, y2, p.N, p.top_k, n, n * kRowsWG, kRowsWG, q.E);
+        my_route = q.sorted[first + min(c, count - 1)];
+        load_a(reinterpret_cast<const uint16_t*>(p.a) + (int64_t)first * K, count);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rb = kEarly; rb < RBW; ++rb) load_w(rb);
+    __builtin_amdgcn_sched_barrier(0);
+    store_scales();
+    sync_lds();
+
+    // 5) fc1: this expert's routes (route r of token r / top_k) as masks over
+    //    the R <= 64 routes, the first sorted position and the route count; a
+    //    workgroup whose expert nobody selected leaves.  The first workgroup
+    //    also writes every expert's offsets and sorted routes for fc2 and the
+    //    combine.
+    uint64_t mine = 0;
+    if constexpr (FC1) {
+        const int R = q.T * p.top_k;
+        const int ex = lane < R ? s_e[lane] : -1;
+        mine = __ballot(ex == e);
+        first = __popcll(__ballot(lane < R && ex < e));
+        count = __popcll(mine);
+        if (count == 0) return;  // whole workgroup; its loads drain on their own
+        if (blockIdx.x == 0 && wave == 0) {
+            if (lane < R) {
+                int less = 0, same_before = 0;
+                for (int r = 0; r < R; ++r) {
+                    const int o = s_e[r];
+                    less += o < ex;
+                    same_before += (o == ex) & (r < lane);
+                }
+                q.sorted[less + same_before] = lane;
+            }
+            if (lane < q.E) {
+                int less = 0;
+                for (int r = 0; r < R; ++r) less += s_e[r] < lane;
+                q.offsets[lane] = less;
+            }
+            if (lane == 0) q.offsets[q.E] = R;
+        }
+    }
+
+    // 6) A fragments through the wavefront's own LDS region (no other
+    //    wavefront reads it) into the MFMA register order; RAW: the
+    //    corrections of MFMA rows 4g..4g+3 per super-step,
+    //    -sum_k (b_r(k) + zp) a_k, from the lane's per-register sums (v_dot2
+    //    with ones), added over the four lane groups
+    store_a();
+    u32x4 afr[S][4];
+    f32x4 corr[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        uint32_t in[16], out[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(a_mine + c * kAPitch + 64 * s + 16 * g + 4 * i);
+            in[4 * i + 0] = v.x;
+            in[4 * i + 1] = v.y;
+            in[4 * i + 2] = v.z;
+            in[4 * i + 3] = v.w;
+        }
+        permute_span<O>(in, out);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) afr[s][t] = u32x4{out[4 * t], out[4 * t + 1], out[4 * t + 2], out[4 * t + 3]};
+        if constexpr (RAW) {
+            float part = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float cls = 0.f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) cls = dot2_sum<DT>(out[4 * t + r], cls);
+                part += -(raw_base<DT, BITS>(r) + zp) * cls;
+            }
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) corr[s][i] = __shfl(part, 4 * g + i);
+        }
+    }
+
+    // 7) the row blocks in order, each as soon as its bytes land
+    const uint16_t* sc_mine = sc_tab + (16 * RBW * rw + c) * kScPitch;
+    f32x4 acc[RBW];
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+        Span<BITS> spn[S];
+        if constexpr (kSliceB == 32) {
+            spn[0].w[0] = wraw[rb][0].x;
+            spn[0].w[1] = wraw[rb][0].y;
+        } else if constexpr (BITS == 2) {
+            spans_of_slice(wraw[rb][0], spn[0], spn[1]);
+        } else {
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) spn[s].w[d] = wraw[rb][s][d];
+        }
+        acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int blk = (k0 + kSuperK * s + (RAW ? 0 : 32 * g)) >> bs_shift;
+            const float scale = Dt<DT>::to_float(sc_mine[rb * 16 * kScPitch + blk]);
+            if constexpr (RAW) {
+                f32x4 part = corr[s];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    part = Dt<DT>::mfma(afr[s][t], raw_step_based<DT, BITS>(spn[s], t, magic), part);
+                acc[rb] += part * scale;
+            } else {
+                BlockParams bq;
+                bq.zp = zp;
+                bq.scale = scale;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    acc[rb] = Dt<DT>::mfma(afr[s][t], dequant_zp<DT, BITS, kZpConst>(spn[s], t, bq), acc[rb]);
+            }
+        }
+        // row block rb + 1's unpacking may not be hoisted above this block's
+        // MFMAs: it would wait for bytes that arrive later
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // 8) partial tiles over the wavefront's own A region (its fragment reads
+    //    are done: LDS accesses of a wavefront complete in order): lane (g, c)
+    //    holds MFMA rows 4g..4g+3 of column c
+    float* const part_mine = reinterpret_cast<float*>(a_mine);
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part_mine[(rb * kRowsA + 4 * g + i) * 16 + c] = acc[rb][i];
+    if constexpr (!FC1) {
+        if (wave == 0 && lane < kRowsA) s_route[lane] = my_route;
+    }
+    sync_lds();
+
+    // 9) epilogue: sums over the K slices in slice order; row block b of the
+    //    workgroup belongs to wavefronts rw = b / RBW (block b % RBW)
+    auto partial = [&](int k, int b, int m, int col) -> const float* {
+        return reinterpret_cast<const float*>(a_reg[(b / RBW) * KSW + k]) + ((b % RBW) * kRowsA + m) * 16 + col;
+    };
+    if constexpr (FC1) {
+        // weight rows 2j (gate) and 2j+1 (up) of activation column j
+        constexpr int kCols = kRowsWG / 2;
+        const int I = p.N / 2;
+        for (int i = tid; i < kRowsA * kCols; i += kThreadsS) {
+            const int m = i / kCols;
+            const int j = i - m * kCols;
+            // token m's route to this expert: the set bit of `mine` among its
+            // top_k routes; its sorted position counts the expert's earlier routes
+            if (m >= q.T) break;
+            const uint64_t slots = (mine >> (m * p.top_k)) & ((p.top_k >= 64 ? 0ull : (1ull << p.top_k)) - 1ull);
+            if (slots == 0) continue;
+            const int r = m * p.top_k + __builtin_ctzll(slots);
+            const int pos = first + __popcll(mine & ((1ull << r) - 1ull));
+            float gate = 0.f, up = 0.f;
+#pragma unroll
+            for (int k = 0; k < KSW; ++k) {
+                const float2 v = *reinterpret_cast<const float2*>(partial(k, (2 * j) >> 4, m, (2 * j) & 15));
+                gate += v.x;
+                up += v.y;
+            }
+            act_out[(int64_t)pos * I + n * kCols + j] = Dt<DT>::from_float(act_value<DT>(act, gate, up, p.ap));
+        }
+    } else {
+        const bool through = p.fused.counters != nullptr;
+        for (int i = tid; i < count * kRowsWG; i += kThreadsS) {
+            const int m = i / kRowsWG;
+            const int r = i - m * kRowsWG;
+            float v = 0.f;
+#pragma unroll
+            for (int k = 0; k < KSW; ++k) v += *partial(k, r >> 4, m, r & 15);
+            store_y2(&y2[(int64_t)s_route[m] * p.N + n * kRowsWG + r], v, through);
+        }
+        if (through) fc2_arrive_combine<DT>(p.fused, y2, p.N, p.top_k, n, n * kRowsWG, kRowsWG, q.E);
     }
 }
 
-
-template <bool FC1, int DT, int BITS, int KS, int P, bool RAW>
+// K slices of 64 bytes per weight row (32 at one 2-bit super-step, 128 at
+// 4 bits over 2048 inputs): super-steps per wavefront S and wavefronts per
+// row KSW (KSW * S = K / 128); row blocks per wavefront so that a workgroup
+// holds 64 weight rows (128 with one wavefront per row).
+template <bool FC1, int DT, int BITS, bool RAW, int S, int KSW>
 hipError_t run(const ProjLaunch& p, const DecodePlan& plan, hipStream_t s)
 {
-    const int rows_wg = 16 * kWavesS / KS;
-    launch(stream_kernel<DT, BITS, FC1, KS, P, RAW>, dim3((unsigned)(plan.E * (p.N / rows_wg))),
-           dim3(kThreadsS), s, p, plan);
+    constexpr int RBW = KSW >= 2 ? KSW / 2 : 1;
+    constexpr int kRowsWG = 16 * (kWavesS / KSW) * RBW;
+    if (p.N % kRowsWG) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(plan.E * (p.N / kRowsWG)));
+    // A rows: an expert has at most T rows; fc1 routes four tokens per
+    // wavefront when every expert fits 16 lanes
+    const bool group = FC1 && plan.E <= 16;
+    if (plan.T <= 8) {
+        if (group) launch(stream_kernel<DT, BITS, FC1, S, KSW, RBW, 8, FC1, RAW>, grid, dim3(kThreadsS), s, p, plan);
+        else launch(stream_kernel<DT, BITS, FC1, S, KSW, RBW, 8, false, RAW>, grid, dim3(kThreadsS), s, p, plan);
+    } else {
+        if (group) launch(stream_kernel<DT, BITS, FC1, S, KSW, RBW, 16, FC1, RAW>, grid, dim3(kThreadsS), s, p, plan);
+        else launch(stream_kernel<DT, BITS, FC1, S, KSW, RBW, 16, false, RAW>, grid, dim3(kThreadsS), s, p, plan);
+    }
     return hipGetLastError();
 }
 
-template <bool FC1, int DT, int BITS, int KS, bool RAW>
-hipError_t launch_pieces(const ProjLaunch& p, const DecodePlan& plan, hipStream_t s)
-{
-    const int pieces = (p.K / KS * BITS / 8 + kLine - 1) / kLine;
-    if (pieces <= 1) return run<FC1, DT, BITS, KS, 1, RAW>(p, plan, s);
-    if (pieces <= 2) return run<FC1, DT, BITS, KS, 2, RAW>(p, plan, s);
-    if (pieces <= 4) return run<FC1, DT, BITS, KS, 4, RAW>(p, plan, s);
-    if constexpr (BITS == 4 && KS == 1) {
-        if (pieces <= 8) return run<FC1, DT, BITS, KS, 8, RAW>(p, plan, s);
-    }
-    return hipErrorInvalidValue;
-}
-
 template <bool FC1, int DT, int BITS, bool RAW>
-hipError_t launch_split(const ProjLaunch& p, const DecodePlan& plan, hipStream_t s)
+hipError_t launch_slices(const ProjLaunch& p, const DecodePlan& plan, hipStream_t s)
 {
-    if constexpr (!FC1) {
-        if (p.K % (2 * kSuperK) == 0) return launch_pieces<FC1, DT, BITS, 2, RAW>(p, plan, s);
+    const int supers = p.K / kSuperK;
+    if constexpr (BITS == 2) {
+        switch (supers) {
+        case 1: return run<FC1, DT, BITS, RAW, 1, 1>(p, plan, s);
+        case 2: return run<FC1, DT, BITS, RAW, 2, 1>(p, plan, s);
+        case 4: return run<FC1, DT, BITS, RAW, 2, 2>(p, plan, s);
+        case 8: return run<FC1, DT, BITS, RAW, 2, 4>(p, plan, s);
+        case 16: return run<FC1, DT, BITS, RAW, 2, 8>(p, plan, s);
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (supers) {
+        case 1: return run<FC1, DT, BITS, RAW, 1, 1>(p, plan, s);
+        case 2: return run<FC1, DT, BITS, RAW, 1, 2>(p, plan, s);
+        case 4: return run<FC1, DT, BITS, RAW, 1, 4>(p, plan, s);
+        case 8: return run<FC1, DT, BITS, RAW, 1, 8>(p, plan, s);
+        case 16: return run<FC1, DT, BITS, RAW, 2, 8>(p, plan, s);
+        default: return hipErrorInvalidValue;
+        }
     }
-    return launch_pieces<FC1, DT, BITS, 1, RAW>(p, plan, s);
 }
 
 template <bool FC1, int DT>
@@ -501,11 +545,10 @@ hipError_t launch_stream(const ProjLaunch& p, const DecodePlan& plan, hipStream_
     if (!stream_fits(p.w, p.K, p.N, p.block_size, FC1)) return hipErrorInvalidValue;
     const bool raw = p.block_size % kSuperK == 0;
     if (p.w.bits == 2) {
-        return raw ? launch_split<FC1, DT, 2, true>(p, plan, s) : launch_split<FC1, DT, 2, false>(p, plan, s);
+        return raw ? launch_slices<FC1, DT, 2, true>(p, plan, s) : launch_slices<FC1, DT, 2, false>(p, plan, s);
     }
-    return raw ? launch_split<FC1, DT, 4, true>(p, plan, s) : launch_split<FC1, DT, 4, false>(p, plan, s);
+    return raw ? launch_slices<FC1, DT, 4, true>(p, plan, s) : launch_slices<FC1, DT, 4, false>(p, plan, s);
 }
-
 
 }  // namespace
 
@@ -513,9 +556,11 @@ bool stream_fits(const ProjArgs& w, int K, int N, int block_size, bool fc1)
 {
     (void)fc1;
     const int bs = block_size;
+    const int supers = K / kSuperK;
+    // whole 8-block scale units per row (16-byte aligned) for the scale table
     return (w.bits == 2 || w.bits == 4) && w.zp == nullptr && K <= kMaxK && K % kSuperK == 0 &&
-           N % (16 * kWavesS) == 0 && bs >= 32 && (bs & (bs - 1)) == 0 && (K / bs) % 8 == 0 &&
-           K / bs <= kMaxBlocks && reinterpret_cast<uintptr_t>(w.scales) % 16 == 0 &&
+           (supers & (supers - 1)) == 0 && N % 128 == 0 && bs >= 32 && (bs & (bs - 1)) == 0 &&
+           (K / bs) % 8 == 0 && reinterpret_cast<uintptr_t>(w.scales) % 16 == 0 &&
            (bs % kSuperK == 0 || w.fast);  // RAW takes any constant zero point
 }
 

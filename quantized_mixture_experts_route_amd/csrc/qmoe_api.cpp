@@ -554,9 +554,8 @@ int qmoe_forward_ex(const void* hidden, const float* logits, int64_t T, int32_t 
     // Chosen when every expert is likely selected, K fits one chunk and fc1's
     // block of weights fits the kernel's LDS staging (2-bit codes, no
     // zero-point tensor: the other variants run out of registers).
-    // Streamed decode (at most 16 tokens and 64 routes): the same idea with every
-    // wavefront owning whole weight rows and consuming its weights piece by
-    // piece as they arrive.
+    // Streamed decode (at most 16 tokens and 64 routes): a workgroup per
+    // (expert, block of weight rows), its wavefronts splitting K.
     const bool stream_mode = !generic && L.decode && T <= 16 && R <= 64 && E <= 64 && E <= R &&
                              qmoe::stream_fits(w1, H, 2 * I, block_size, true) &&
                              qmoe::stream_fits(w2, I, H, block_size, false);

@@ -125,4 +125,59 @@ __device__ inline void route_token(const float* row, int E, int top_k, int norma
                       agg);
 }
 
+// Several tokens per wavefront: L lanes per token (L = 8 or 16, E <= L),
+// lane L*i + j holding expert j of token i of the wavefront.  The same
+// selection and arithmetic as route_values (the total-order key with the
+// lowest index on ties, m the largest non-NaN logit, exp(l - m) summed in
+// slot order), with every reduction confined to the token's L lanes by DPP
+// (quad permutes, the 8-lane mirror, for L = 16 the 16-lane mirror); sums
+// pair the lanes in the order route_values pairs them, and the lanes it adds
+// beyond E hold zeros, so the weights are bit for bit route_values'.  No
+// router_weights.  Lane L*i + s (s < top_k) calls emit(s, expert, weight);
+// every lane must be active and `v` is ignored where j >= E.
+template <int L, class Emit>
+__device__ inline void route_group(int E, int top_k, int normalize, float v, Emit emit)
+{
+    static_assert(L == 8 || L == 16, "lanes per token");
+    const int j = threadIdx.x & (L - 1);
+    const bool ok = j < E;
+    auto gmax64 = [](uint64_t x) {
+        x = max_u64(x, dpp_u64<kDppXor1>(x));
+        x = max_u64(x, dpp_u64<kDppXor2>(x));
+        x = max_u64(x, dpp_u64<kDppHalfMirror>(x));
+        if constexpr (L == 16) x = max_u64(x, dpp_u64<kDppMirror>(x));
+        return x;
+    };
+    float m = (ok && v > -INFINITY) ? v : -INFINITY;  // NaN compares false and is skipped
+    m = f32_max(m, dpp_f32<kDppXor1>(m));
+    m = f32_max(m, dpp_f32<kDppXor2>(m));
+    m = f32_max(m, dpp_f32<kDppHalfMirror>(m));
+    if constexpr (L == 16) m = f32_max(m, dpp_f32<kDppMirror>(m));
+    const uint32_t ukey = (uint32_t)route_key(v) ^ 0x80000000u;
+    uint64_t cand = ok ? (((uint64_t)ukey << 32) | (uint32_t)~(uint32_t)j) : 0;
+    int my_id = 0;
+    float my_num = 0.0f, den = 0.0f;
+    for (int s = 0; s < top_k; ++s) {
+        const uint64_t best = gmax64(cand);  // words are distinct: each holds its expert index
+        const int e = (int)~(uint32_t)best;
+        const float bv = key_to_logit((int32_t)((uint32_t)(best >> 32) ^ 0x80000000u));
+        const float num = expf(bv - m);
+        if (normalize) den += num;  // slot order
+        if (j == e) cand = 0;
+        if (j == s) {
+            my_id = e;
+            my_num = num;
+        }
+    }
+    if (!normalize) {
+        float part = ok ? expf(v - m) : 0.0f;
+        part += dpp_f32<kDppXor1>(part);
+        part += dpp_f32<kDppXor2>(part);
+        part += dpp_f32<kDppHalfMirror>(part);
+        if constexpr (L == 16) part += dpp_f32<kDppMirror>(part);
+        den = part;
+    }
+    if (j < top_k) emit(j, my_id, my_num / den);
+}
+
 }  // namespace qmoe

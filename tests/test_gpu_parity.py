@@ -198,6 +198,10 @@ def _layer_check(spec, seed, tokens=None, logits=None):
     torch.cuda.synchronize()
     ids_ref, w_ref = oracle.route(inp["logits"], spec["k"], spec["normalize"])
     assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    # the routing weights every path writes: fp32 expf (<= 2 ulp), a sum of
+    # k (normalize) or E terms, one division
+    rtol = (max(spec["k"], spec["E"]) + 6) * U
+    np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=rtol, atol=0)
     ref = oracle.forward(inp, spec, tokens)
     got = dv.as_f64(out)
     if tokens is not None:
@@ -348,6 +352,23 @@ STREAM = [
     dict(T=9, H=2048, I=1024, E=16, k=7, fc1_bits=4, fc2_bits=2, block_size=128, dtype=1, act=1,
          zp_mode="sym", zpo=math.nan),
 ]
+
+
+@pytest.mark.parametrize("E,k,normalize", [(16, 3, 1), (16, 4, 0), (5, 2, 1), (9, 4, 0), (12, 1, 1)])
+def test_layer_stream_decode_routing_ties(E, k, normalize):
+    # streamed decode with every expert in 16 lanes (four tokens routed per
+    # wavefront): logits with many ties, signed zeros and a row of equal values;
+    # ids exact, weights and outputs against the oracle (E <= T*k <= 64)
+    T = 16 if E > 8 else 8
+    rng = np.random.default_rng(1700 + E * 10 + k)
+    logits = np.round(rng.standard_normal((T, E)) * 1.5).astype(np.float32)
+    logits[0, :] = 0.25
+    logits[1, :] = -0.0
+    logits[1, E // 2] = 0.0
+    spec = synth.custom(T=T, H=1024, I=1024, E=E, k=k, fc1_bits=2, fc2_bits=4, block_size=128, dtype=1 + E % 2,
+                        act=k % 2, normalize=normalize, zp_mode="zpo", zpo=1.5,
+                        name=f"stream_ties_E{E}_k{k}_n{normalize}")
+    _layer_check(spec, 1360 + E + k, logits=logits)
 
 
 @pytest.mark.parametrize("case", range(len(STREAM)))
