@@ -120,10 +120,7 @@ __device__ inline float act_value(int act, float gate, float up, const ActParams
     if (act == kGeGLU) return gated<kGeGLU>(gate, up);
     const float g = fminf(gate, ap.limit);
     const float u = isnan(up) ? up : fminf(fmaxf(up, -ap.limit), ap.limit);
-    const float z = ap.alpha * g;
-    const float e = expf(-fabsf(z));
-    const float sig = z >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
-    return g * sig * (u + ap.beta);
+    return g * sigmoid_fast(ap.alpha * g) * (u + ap.beta);
 }
 
 // fc1 (+ fc3) weight row of a gate or up row of activation column j, by the

@@ -533,20 +533,28 @@ __device__ inline u32x4 dequant_step_generic(const Span<BITS>& sp, int t, float 
 }
 
 // ---------------------------------------------------------------- activation
+// sigmoid(z) from e = exp(-|z|) in [0, 1], so that neither sign overflows:
+// 1 / (1 + e) for z >= 0, e / (1 + e) below.  The exponential is the
+// hardware base-2 one (v_exp_f32 of -|z| log2 e) and the quotient a hardware
+// reciprocal (v_rcp_f32), each a few float32 ulps from the exact value; the
+// activation is rounded to fp16/bf16 afterwards.  NaN stays NaN.
+__device__ inline float sigmoid_fast(float z)
+{
+    const float e = __expf(-fabsf(z));
+    return (z >= 0.0f ? 1.0f : e) * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // Gated activations on an interleaved gate/up pair [qmoe.rs qmoe_activate
 // (swiglu_value with alpha 1, beta 0, no limit; tanh-GELU constants);
-// PR 32198 GeGLU].
+// PR 32198 GeGLU].  tanh-GELU uses 0.5 (1 + tanh(x)) = sigmoid(2x).
 template <int ACT>
 __device__ inline float gated(float g, float u)
 {
     if constexpr (ACT == kGeGLU) {
         const float inner = 0.7978845608028654f * (g + 0.044715f * g * g * g);
-        return 0.5f * g * (1.0f + tanhf(inner)) * u;
+        return g * sigmoid_fast(2.0f * inner) * u;
     } else {
-        // sigmoid computed without overflow for either sign of g
-        const float e = expf(-fabsf(g));
-        const float sig = g >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
-        return g * sig * u;
+        return g * sigmoid_fast(g) * u;
     }
 }
 
