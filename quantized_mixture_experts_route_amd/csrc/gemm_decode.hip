@@ -383,8 +383,10 @@ constexpr int kRowsItem = kWaves * kRowsWave;  // weight rows per workgroup
 constexpr int kRowsScUnits = kRowsItem * (kChunkK / 32 / 8) / kThreads;  // 16-byte scale units per thread
 constexpr int kDppRotate8 = 0x128;  // DPP row_ror:8: lane c reads lane c ^ 8 of its row
 
+// (The 16-row A tile and the scale table take 83 KB of LDS, one workgroup
+// per CU, so that form runs two wavefronts per SIMD whatever its registers.)
 template <int DT, int BITS, bool FC1, int ZP, int MTR, int SS>
-__global__ __launch_bounds__(kThreads, 4) void decode_rows_kernel(ProjLaunch p,
+__global__ __launch_bounds__(kThreads, MTR == 16 ? 2 : 4) void decode_rows_kernel(ProjLaunch p,
                                                                   const int32_t* __restrict__ tiles,
                                                                   const int32_t* __restrict__ n_tiles_ptr)
 {

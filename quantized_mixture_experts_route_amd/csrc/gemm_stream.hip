@@ -123,8 +123,23 @@ __device__ inline void spans_of_slice(const u32x4& v, Span<2>& s0, Span<2>& s1)
     }
 }
 
+// LDS of a workgroup (the wavefronts' A regions and the scale table), and
+// the wavefronts per SIMD its registers are sized for: four (two workgroups
+// per CU) unless the LDS or RBW = 8's registers leave room for one.
+template <int S, int KSW, int RBW, bool RAW>
+constexpr int stream_lds_bytes()
+{
+    return kWavesS * kRowsA * (S * kSuperK / 2 + 4) * 4 +
+           16 * (kWavesS / KSW) * RBW * ((RAW ? kMaxK / kSuperK : kMaxK / 32) + 2) * 2;
+}
+template <int S, int KSW, int RBW, bool RAW>
+constexpr int stream_waves()
+{
+    return RBW <= 4 && 2 * (stream_lds_bytes<S, KSW, RBW, RAW>() + 1024) <= 160 * 1024 ? 4 : 2;
+}
+
 template <int DT, int BITS, bool FC1, int S, int KSW, int RBW, int AR, bool GR, bool RAW>
-__global__ __launch_bounds__(kThreadsS, RBW <= 4 ? 4 : 2) void stream_kernel(ProjLaunch p, DecodePlan q)
+__global__ __launch_bounds__(kThreadsS, (stream_waves<S, KSW, RBW, RAW>())) void stream_kernel(ProjLaunch p, DecodePlan q)
 {
     constexpr int RW = kWavesS / KSW;              // wavefronts along the rows
     constexpr int kBlocksWG = RW * RBW;            // 16-row weight blocks per workgroup
@@ -149,6 +164,7 @@ __global__ __launch_bounds__(kThreadsS, RBW <= 4 ? 4 : 2) void stream_kernel(Pro
     __shared__ __attribute__((aligned(16))) uint16_t sc_tab[kRowsWG * kScPitch];
     __shared__ int s_e[kMaxRoutesS];  // fc1: expert of route r
     __shared__ int s_route[kRowsA];   // fc2: route id of the expert's row m
+    static_assert(sizeof(a_reg) + sizeof(sc_tab) == stream_lds_bytes<S, KSW, RBW, RAW>(), "LDS estimate");
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

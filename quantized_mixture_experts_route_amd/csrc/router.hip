@@ -59,7 +59,6 @@ __global__ __launch_bounds__(kThreadsR) void router_kernel(const uint16_t* __res
         const int s_hi = steps * (ks + 1) / split;
         const uint16_t* wb = w + (int64_t)min(eb * 16 + c, E - 1) * H + 8 * g;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
         for (int s = s_lo; s < s_hi; ++s) {
             const u32x4 a = *reinterpret_cast<const u32x4*>(xa + 32 * s);
             const u32x4 b = *reinterpret_cast<const u32x4*>(wb + 32 * s);
