@@ -413,7 +413,9 @@ int64_t persistent_grid(Kernel kernel, int threads, int64_t item_bound)
 inline bool can_stage(const ProjLaunch& p, bool fc1)
 {
     const int parts = fc1 ? 1 : p.k_split;
-    return p.block_size >= 32 && (p.K / parts / p.block_size) % 8 == 0 &&
+    // a K part holds a whole number (at least one) of 8-block stages; a part
+    // shorter than a block has no stage of its own
+    return p.block_size >= 32 && (p.K / parts) % (8 * p.block_size) == 0 &&
            reinterpret_cast<uintptr_t>(p.w.scales) % 16 == 0;
 }
 

@@ -496,7 +496,7 @@ int qmoe_forward_ex(const void* hidden, const float* logits, int64_t T, int32_t 
     // 16-byte aligned) and it still yields a few items per CU
     const qmoe::ProjArgs w1 = proj_args(fc1, zero_point_offset);
     const qmoe::ProjArgs w2 = proj_args(fc2, zero_point_offset);
-    const bool stageable = (H / block_size) % 8 == 0 && (I / block_size) % 8 == 0 &&
+    const bool stageable = H % (8 * block_size) == 0 && I % (8 * block_size) == 0 &&
                            aligned(w1.scales, 16) && aligned(w2.scales, 16);
     if (!L.decode && block_size >= 32 && w1.fast && w2.fast && stageable && !wide_codes &&
         (T * top_k / qmoe::kPrefillMTLarge) * ceil_div(I, qmoe::prefill_fc1_cols(qmoe::kPrefillMTLarge)) >= 1024) {
@@ -529,7 +529,7 @@ int qmoe_forward_ex(const void* hidden, const float* logits, int64_t T, int32_t 
     // stages its scales) whole 8-block scale stages
     int k_split = L.decode ? 1 : fc2_split(R, E, H, I, L.m_tile, L.nbw);
     while (k_split > 1 && (I % (k_split * qmoe::kSuperK) ||
-                           (L.m_tile == qmoe::kPrefillMTLarge && (I / k_split / block_size) % 8))) {
+                           (L.m_tile == qmoe::kPrefillMTLarge && (I / k_split) % (8 * block_size)))) {
         k_split /= 2;
     }
     if (k_split > L.k_split_cap) k_split = L.k_split_cap;

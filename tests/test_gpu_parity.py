@@ -296,6 +296,19 @@ def test_layer_mid_prefill_tile(dtype, bits, zp, bs):
     _layer_check(spec, 700 + bs, tokens=tokens)
 
 
+@pytest.mark.parametrize("I,bs", [(256, 256), (512, 512)])
+def test_layer_prefill_fc2_parts_shorter_than_a_block(I, bs):
+    # 700 routes over 256 experts leave fc2's work-list short enough that its K
+    # is split in two parts, each shorter than one quantization block: both
+    # parts take the block's scale (no staged scale table of whole 8-block
+    # stages exists for them)
+    spec = synth.custom(T=100, H=1024, I=I, E=256, k=7, fc1_bits=4, fc2_bits=2, block_size=bs,
+                        dtype=2, act=0, normalize=0, zp_mode="zpo", zpo=1.5,
+                        name=f"short_parts_I{I}_bs{bs}")
+    tokens = np.unique(np.concatenate([np.linspace(0, 99, 20).astype(np.int64), [1, 98]]))
+    _layer_check(spec, 1300 + bs, tokens=tokens)
+
+
 @pytest.mark.parametrize("T", [3, 70])
 def test_layer_block_size_16(T):
     # 16-input blocks: each 32-code span holds two blocks (decode T=3, prefill T=70)
