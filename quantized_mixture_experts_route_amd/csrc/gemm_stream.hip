@@ -340,10 +340,10 @@ __global__ __launch_bounds__(kThreadsS, (stream_waves<S, KSW, RBW, RAW>())) void
     sync_lds();
 
     // 5) fc1: this expert's routes (route r of token r / top_k) as masks over
-    //    the R <= 64 routes, the first sorted position and the route count; a
-    //    workgroup whose expert nobody selected leaves.  The first workgroup
-    //    also writes every expert's offsets and sorted routes for fc2 and the
-    //    combine.
+    //    the R <= 64 routes, the first sorted position and the route count.
+    //    The first workgroup writes every expert's offsets and sorted routes
+    //    for fc2 and the combine (also when its own expert has none); then a
+    //    workgroup whose expert nobody selected leaves.
     uint64_t mine = 0;
     if constexpr (FC1) {
         const int R = q.T * p.top_k;
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(kThreadsS, (stream_waves<S, KSW, RBW, RAW>())) void
         mine = __ballot(ex == e);
         first = __popcll(__ballot(lane < R && ex < e));
         count = __popcll(mine);
-        if (count == 0) return;  // whole workgroup; its loads drain on their own
+        // the writer writes before it may leave: its own expert can have no routes
         if (blockIdx.x == 0 && wave == 0) {
             if (lane < R) {
                 int less = 0, same_before = 0;
@@ -369,6 +369,7 @@ __global__ __launch_bounds__(kThreadsS, (stream_waves<S, KSW, RBW, RAW>())) void
             }
             if (lane == 0) q.offsets[q.E] = R;
         }
+        if (count == 0) return;  // whole workgroup; its loads drain on their own
     }
 
     // 6) A fragments through the wavefront's own LDS region (no other

@@ -333,7 +333,7 @@ def test_layer_decode_expert_stationary(T, k, E, skew):
     _layer_check(spec, 40 + T + E, logits=logits)
 
 
-# Streamed decode: R = T*top_k <= 16, E <= R, 2/4-bit widths, K <= 2048 with
+# Streamed decode: R = T*top_k <= 64, E <= R or E <= 16, 2/4-bit widths, K <= 2048 with
 # whole 8-block scale units per row; cases cover both widths per projection,
 # RAW (block multiple of 128) and per-element dequant, one piece with a
 # clamped tail (K = 256 at 2 bits), eight pieces (4 bits, K = 2048), A rows
@@ -397,6 +397,22 @@ def test_layer_stream_decode_one_expert_sixteen_rows():
     logits = np.zeros((16, 2), dtype=np.float32)
     logits[:, 0] = 2.0
     _layer_check(spec, 1350, logits=logits)
+
+
+@pytest.mark.parametrize("T,E,k", [(8, 8, 2), (1, 8, 2), (3, 8, 2), (4, 16, 2), (16, 32, 4)])
+def test_layer_stream_decode_expert_zero_unselected(T, E, k):
+    # the first workgroup of the streamed fc1 writes every expert's offsets
+    # and sorted routes; here its own expert (0) has no route.  A call with
+    # every token on expert 0 runs first, so stale tables from it would show.
+    spec = synth.custom(T=T, H=512, I=256, E=E, k=k, fc1_bits=4, fc2_bits=2, block_size=32, dtype=1,
+                        act=0, zp_mode="sym", name=f"stream_no_e0_T{T}_E{E}")
+    rng = np.random.default_rng(1800 + 7 * T + E)
+    logits = rng.normal(0.0, 1.0, size=(T, E)).astype(np.float32)
+    on_zero = logits.copy()
+    on_zero[:, 0] = 8.0
+    _layer_check(spec, 1800 + T, logits=on_zero)
+    logits[:, 0] = -8.0
+    _layer_check(spec, 1800 + T, logits=logits)
 
 
 # Row-block decode over the m-tile list (more experts than routes, or widths
