@@ -6,8 +6,11 @@ combinations the hand-written cases do not list; a second set adds random
 operator options (gate/up layouts with fc3, biases, router_weights, SwiGLU
 alpha/beta/limit).  Each layer is compared with the oracle on sampled
 tokens (first, last and random ones) at the layer bound of the other parity
-tests.  Sizes are capped so that one case costs well under a second of host
-work."""
+tests.  A third set draws small decode layers (at most 16 tokens and 16
+experts, 2/4-bit, K a power of two up to 2048), often with fewer routes than
+experts, for the streamed decode kernels; every fourth one keeps expert 0
+out of every token's choice.  Sizes are capped so that one case costs well
+under a second of host work."""
 from __future__ import annotations
 
 import math
@@ -23,6 +26,7 @@ pytestmark = pytest.mark.gpu
 
 N_CASES = 48
 N_OPTION_CASES = 24
+N_STREAM_CASES = 24
 
 
 def _draw(i: int) -> tuple[dict, np.ndarray]:
@@ -126,3 +130,37 @@ def test_layer_random_shape_with_options(i):
           f"fusion={spec.get('swiglu_fusion', 1)} bias={spec.get('bias', False)} "
           f"router_weights={spec.get('router_weights', False)}", flush=True)
     _options_check(spec, 8900 + i, tokens=tokens)
+
+
+def _draw_stream(i: int) -> tuple[dict, np.ndarray | None]:
+    rng = np.random.default_rng(5151 + i)
+    bs = int(rng.choice([32, 64, 128, 256]))
+    H = max(bs, int(rng.choice([128, 256, 512, 1024, 2048])))
+    I = max(bs, int(rng.choice([128, 256, 512, 1024, 2048])))
+    E = int(rng.integers(2, 17))
+    T = int(rng.choice([1, 1, 2, 2, 3, 4, 5, 8, 12, 16]))
+    k = int(rng.integers(1, min(E, 4) + 1))
+    b1, b2 = (int(b) for b in rng.choice([2, 4], size=2))
+    zp_mode = str(rng.choice(["sym", "zpo"]))
+    zpo = float(rng.choice([0.5, 1.5, 3.0])) if zp_mode == "zpo" else math.nan
+    if zp_mode == "zpo" and zpo > (1 << min(b1, b2)) - 1:
+        zpo = 0.5
+    s0 = 2.0 / ((1 << (max(b1, b2) - 1)) * math.sqrt(max(H, I)))
+    spec = synth.custom(T=T, H=H, I=I, E=E, k=k, fc1_bits=b1, fc2_bits=b2, block_size=bs,
+                        dtype=int(rng.integers(1, 3)), act=int(rng.integers(0, 2)),
+                        normalize=int(rng.integers(0, 2)), zp_mode=zp_mode, zpo=zpo,
+                        scale_range=(0.5 * s0, 1.5 * s0), name=f"random_stream{i}")
+    logits = None
+    if i % 4 == 3 and k < E:
+        logits = rng.normal(0.0, 1.0, size=(T, E)).astype(np.float32)
+        logits[:, 0] = -8.0
+    return spec, logits
+
+
+@pytest.mark.parametrize("i", range(N_STREAM_CASES))
+def test_layer_random_small_decode(i):
+    spec, logits = _draw_stream(i)
+    print(f"  T={spec['T']} H={spec['H']} I={spec['I']} E={spec['E']} k={spec['k']} "
+          f"bits={spec['fc1_bits']}/{spec['fc2_bits']} bs={spec['block_size']} zp={spec['zp_mode']} "
+          f"expert0_out={logits is not None}", flush=True)
+    _layer_check(spec, 8700 + i, logits=logits)
