@@ -374,8 +374,8 @@ int qmoe_raw_codes(const qmoe_proj* p, int32_t E, int32_t N, int32_t K, int32_t 
  * timer.  Stages: 0 route (on the decode path: routing, grouping and the
  * m-tile list in one kernel), 1 group (prefill path only), 2 fc1
  * (+ activation), 3 fc2, 4 combine (no launch on the streamed decode path,
- * T <= 16 and T*top_k <= 64 with E <= min(T*top_k, 64), whose fc2 launch
- * performs the combine).
+ * T <= 16 and T*top_k <= 64 with E <= T*top_k or E <= 16 and widths and
+ * blocks the streamed kernels take, whose fc2 launch performs the combine).
  */
 #define QMOE_STAGE_ROUTE 0
 #define QMOE_STAGE_GROUP 1
