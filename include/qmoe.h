@@ -374,7 +374,7 @@ int qmoe_raw_codes(const qmoe_proj* p, int32_t E, int32_t N, int32_t K, int32_t 
  * timer.  Stages: 0 route (on the decode path: routing, grouping and the
  * m-tile list in one kernel), 1 group (prefill path only), 2 fc1
  * (+ activation), 3 fc2, 4 combine (no launch on the streamed decode path,
- * T <= 16 and T*top_k <= 64 with E <= T*top_k or E <= 16 and widths and
+ * T <= 16 and T*top_k <= 64 with E <= T*top_k or E <= 32 and widths and
  * blocks the streamed kernels take, whose fc2 launch performs the combine).
  */
 #define QMOE_STAGE_ROUTE 0

@@ -138,7 +138,11 @@ constexpr int stream_waves()
     return RBW <= 4 && 2 * (stream_lds_bytes<S, KSW, RBW, RAW>() + 1024) <= 160 * 1024 ? 4 : 2;
 }
 
-template <int DT, int BITS, bool FC1, int S, int KSW, int RBW, int AR, bool GR, bool RAW>
+// RF (route first, for layers with more experts than routes): a workgroup
+// learns whether anyone selected its expert before it requests any weight
+// byte, so unselected experts cost no HBM traffic; otherwise the weights are
+// requested first and routing overlaps their latency.
+template <int DT, int BITS, bool FC1, int S, int KSW, int RBW, int AR, bool GR, bool RAW, bool RF>
 __global__ __launch_bounds__(kThreadsS, (stream_waves<S, KSW, RBW, RAW>())) void stream_kernel(ProjLaunch p, DecodePlan q)
 {
     constexpr int RW = kWavesS / KSW;              // wavefronts along the rows
@@ -244,12 +248,13 @@ __global__ __launch_bounds__(kThreadsS, (stream_waves<S, KSW, RBW, RAW>())) void
     const int upr = n_blocks >> 3;  // units per row (n_blocks is a multiple of 8)
     const int n_units = kRowsWG * upr;
     u32x4 sc_unit[kScUnits];
+    auto load_scales = [&]() {
 #pragma unroll
-    for (int k = 0; k < kScUnits; ++k) {
-        const int u = min(tid + kThreadsS * k, n_units - 1);
-        sc_unit[k] = *reinterpret_cast<const u32x4*>(sc_src + 8 * u);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+        for (int k = 0; k < kScUnits; ++k) {
+            const int u = min(tid + kThreadsS * k, n_units - 1);
+            sc_unit[k] = *reinterpret_cast<const u32x4*>(sc_src + 8 * u);
+        }
+    };
 
     // weight row block rb: lane (g, c) reads bytes [16g, 16g+16) of row
     // wr0 + 16 rb + c's slice (and [64+16g, ...) for a 128-byte slice; a
@@ -264,10 +269,6 @@ __global__ __launch_bounds__(kThreadsS, (stream_waves<S, KSW, RBW, RAW>())) void
             wraw[rb][i] = *reinterpret_cast<const WLoad*>(w_row + rb * 16 * row_bytes + 64 * i +
                                                           (kSliceB == 32 ? 8 : 16) * g);
     };
-
-#pragma unroll
-    for (int rb = 0; rb < kEarly; ++rb) load_w(rb);
-    __builtin_amdgcn_sched_barrier(0);
 
     auto store_scales = [&]() {
 #pragma unroll
@@ -287,39 +288,100 @@ __global__ __launch_bounds__(kThreadsS, (stream_waves<S, KSW, RBW, RAW>())) void
     // 3) fc1: route every token (GR: four tokens per wavefront, so the first
     //    T / 4 wavefronts route; otherwise one wavefront per token); the
     //    other wavefronts go on to their A fragments
-    if constexpr (FC1) {
-        const bool writer = blockIdx.x == 0;
-        // the fc2 launch's column-block counters start at zero
-        if (writer && tid < q.n_counters) {
-            __hip_atomic_store(&q.counters[tid], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        auto emit_for = [&](int t) {
-            return [&, t](int slot, int ex, float w) {
-                if (t >= q.T) return;
-                const int r = t * p.top_k + slot;
-                s_e[r] = ex;
-                if (writer) {
-                    q.weights[r] = w;
-                    if (q.ids_out) q.ids_out[r] = ex;
-                    if (q.w_out) q.w_out[r] = w;
-                }
+    auto route_all = [&]() {
+        if constexpr (FC1) {
+            const bool writer = blockIdx.x == 0;
+            // the fc2 launch's column-block counters start at zero
+            if (writer && tid < q.n_counters) {
+                __hip_atomic_store(&q.counters[tid], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            auto emit_for = [&](int t) {
+                return [&, t](int slot, int ex, float w) {
+                    if (t >= q.T) return;
+                    const int r = t * p.top_k + slot;
+                    s_e[r] = ex;
+                    if (writer) {
+                        q.weights[r] = w;
+                        if (q.ids_out) q.ids_out[r] = ex;
+                        if (q.w_out) q.w_out[r] = w;
+                    }
+                };
             };
-        };
-        if constexpr (GR) {
-            if (kGroupTok * wave < q.T) {
-                route_group<16>(q.E, p.top_k, q.normalize, lg[0], emit_for(kGroupTok * wave + (lane >> 4)));
-            }
-        } else {
+            if constexpr (GR) {
+                if (kGroupTok * wave < q.T) {
+                    route_group<16>(q.E, p.top_k, q.normalize, lg[0], emit_for(kGroupTok * wave + (lane >> 4)));
+                }
+            } else {
 #pragma unroll
-            for (int j = 0; j < kTokW; ++j) {
-                const int t = wave + kWavesS * j;
-                if (t >= q.T) break;
-                route_values<1>(q.E, p.top_k, q.normalize, [&](int) { return lg[j]; }, emit_for(t));
+                for (int j = 0; j < kTokW; ++j) {
+                    const int t = wave + kWavesS * j;
+                    if (t >= q.T) break;
+                    route_values<1>(q.E, p.top_k, q.normalize, [&](int) { return lg[j]; }, emit_for(t));
+                }
             }
         }
-    } else {
-        if (count == 0) {  // no rows of this expert: arrive on the column block only
+    };
+    // 5) fc1: this expert's routes (route r of token r / top_k) as masks over
+    //    the R <= 64 routes, the first sorted position and the route count.
+    //    The first workgroup writes every expert's offsets and sorted routes
+    //    for fc2 and the combine (also when its own expert has none); then a
+    //    workgroup whose expert nobody selected leaves.
+    uint64_t mine = 0;
+    auto rank_and_write = [&]() {
+        if constexpr (FC1) {
+            const int R = q.T * p.top_k;
+            const int ex = lane < R ? s_e[lane] : -1;
+            mine = __ballot(ex == e);
+            first = __popcll(__ballot(lane < R && ex < e));
+            count = __popcll(mine);
+            // the writer writes before it may leave: its own expert can have no routes
+            if (blockIdx.x == 0 && wave == 0) {
+                if (lane < R) {
+                    int less = 0, same_before = 0;
+                    for (int r = 0; r < R; ++r) {
+                        const int o = s_e[r];
+                        less += o < ex;
+                        same_before += (o == ex) & (r < lane);
+                    }
+                    q.sorted[less + same_before] = lane;
+                }
+                if (lane < q.E) {
+                    int less = 0;
+                    for (int r = 0; r < R; ++r) less += s_e[r] < lane;
+                    q.offsets[lane] = less;
+                }
+                if (lane == 0) q.offsets[q.E] = R;
+            }
+        }
+    };
+    // fc2: an expert with no rows arrives on the column block only
+    auto fc2_leave = [&]() {
+        if constexpr (!FC1) {
             if (p.fused.counters) fc2_arrive_combine<DT>(p.fused, y2, p.N, p.top_k, n, n * kRowsWG, kRowsWG, q.E);
+        }
+    };
+
+    if constexpr (RF) {  // routes and ranks before the first weight request
+        if constexpr (FC1) {
+            route_all();
+            sync_lds();
+            rank_and_write();
+        }
+        if (count == 0) {  // whole workgroup
+            fc2_leave();
+            return;
+        }
+    }
+    load_scales();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rb = 0; rb < kEarly; ++rb) load_w(rb);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!RF) {
+        if constexpr (FC1) {
+            route_all();
+        } else if (count == 0) {
+            fc2_leave();
             return;
         }
     }
@@ -339,36 +401,8 @@ __global__ __launch_bounds__(kThreadsS, (stream_waves<S, KSW, RBW, RAW>())) void
     store_scales();
     sync_lds();
 
-    // 5) fc1: this expert's routes (route r of token r / top_k) as masks over
-    //    the R <= 64 routes, the first sorted position and the route count.
-    //    The first workgroup writes every expert's offsets and sorted routes
-    //    for fc2 and the combine (also when its own expert has none); then a
-    //    workgroup whose expert nobody selected leaves.
-    uint64_t mine = 0;
-    if constexpr (FC1) {
-        const int R = q.T * p.top_k;
-        const int ex = lane < R ? s_e[lane] : -1;
-        mine = __ballot(ex == e);
-        first = __popcll(__ballot(lane < R && ex < e));
-        count = __popcll(mine);
-        // the writer writes before it may leave: its own expert can have no routes
-        if (blockIdx.x == 0 && wave == 0) {
-            if (lane < R) {
-                int less = 0, same_before = 0;
-                for (int r = 0; r < R; ++r) {
-                    const int o = s_e[r];
-                    less += o < ex;
-                    same_before += (o == ex) & (r < lane);
-                }
-                q.sorted[less + same_before] = lane;
-            }
-            if (lane < q.E) {
-                int less = 0;
-                for (int r = 0; r < R; ++r) less += s_e[r] < lane;
-                q.offsets[lane] = less;
-            }
-            if (lane == 0) q.offsets[q.E] = R;
-        }
+    if constexpr (FC1 && !RF) {
+        rank_and_write();
         if (count == 0) return;  // whole workgroup; its loads drain on their own
     }
 
@@ -507,6 +541,13 @@ __global__ __launch_bounds__(kThreadsS, (stream_waves<S, KSW, RBW, RAW>())) void
     }
 }
 
+template <int DT, int BITS, bool FC1, int S, int KSW, int RBW, int AR, bool GR, bool RAW>
+void launch_rf(bool rf, dim3 grid, hipStream_t s, const ProjLaunch& p, const DecodePlan& plan)
+{
+    if (rf) launch(stream_kernel<DT, BITS, FC1, S, KSW, RBW, AR, GR, RAW, true>, grid, dim3(kThreadsS), s, p, plan);
+    else launch(stream_kernel<DT, BITS, FC1, S, KSW, RBW, AR, GR, RAW, false>, grid, dim3(kThreadsS), s, p, plan);
+}
+
 // K slices of 64 bytes per weight row (32 at one 2-bit super-step, 128 at
 // 4 bits over 2048 inputs): super-steps per wavefront S and wavefronts per
 // row KSW (KSW * S = K / 128); row blocks per wavefront so that a workgroup
@@ -521,12 +562,14 @@ hipError_t run(const ProjLaunch& p, const DecodePlan& plan, hipStream_t s)
     // A rows: an expert has at most T rows; fc1 routes four tokens per
     // wavefront when every expert fits 16 lanes
     const bool group = FC1 && plan.E <= 16;
+    // route first when some experts must go unselected
+    const bool rf = plan.E > plan.T * p.top_k;
     if (plan.T <= 8) {
-        if (group) launch(stream_kernel<DT, BITS, FC1, S, KSW, RBW, 8, FC1, RAW>, grid, dim3(kThreadsS), s, p, plan);
-        else launch(stream_kernel<DT, BITS, FC1, S, KSW, RBW, 8, false, RAW>, grid, dim3(kThreadsS), s, p, plan);
+        if (group) launch_rf<DT, BITS, FC1, S, KSW, RBW, 8, FC1, RAW>(rf, grid, s, p, plan);
+        else launch_rf<DT, BITS, FC1, S, KSW, RBW, 8, false, RAW>(rf, grid, s, p, plan);
     } else {
-        if (group) launch(stream_kernel<DT, BITS, FC1, S, KSW, RBW, 16, FC1, RAW>, grid, dim3(kThreadsS), s, p, plan);
-        else launch(stream_kernel<DT, BITS, FC1, S, KSW, RBW, 16, false, RAW>, grid, dim3(kThreadsS), s, p, plan);
+        if (group) launch_rf<DT, BITS, FC1, S, KSW, RBW, 16, FC1, RAW>(rf, grid, s, p, plan);
+        else launch_rf<DT, BITS, FC1, S, KSW, RBW, 16, false, RAW>(rf, grid, s, p, plan);
     }
     return hipGetLastError();
 }

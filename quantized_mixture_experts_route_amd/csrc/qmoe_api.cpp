@@ -555,13 +555,13 @@ int qmoe_forward_ex(const void* hidden, const float* logits, int64_t T, int32_t 
     // block of weights fits the kernel's LDS staging (2-bit codes, no
     // zero-point tensor: the other variants run out of registers).
     // Streamed decode (at most 16 tokens and 64 routes): a workgroup per
-    // (expert, block of weight rows), its wavefronts splitting K.  Its
-    // workgroups stream their expert's weights before routing is known, so
-    // with fewer routes than experts the unselected experts' bytes are read
-    // for nothing: taken then only up to 16 experts (at one to four tokens,
-    // top-2, 2048 x 2048 int2: faster than the m-tile list up to 16
-    // experts, even at 32, slower at 64).
-    const bool stream_mode = !generic && L.decode && T <= 16 && R <= 64 && (E <= R || E <= 16) &&
+    // (expert, block of weight rows), its wavefronts splitting K.  With
+    // fewer routes than experts its workgroups route before they request
+    // weights, so unselected experts read none; taken then up to 32 experts
+    // (one to eight tokens, top-2, 2048 x 2048 int2: faster than the m-tile
+    // list at 16 and 32 experts, slower at 64, where thousands of workgroups
+    // start only to leave).
+    const bool stream_mode = !generic && L.decode && T <= 16 && R <= 64 && (E <= R || E <= 32) &&
                              qmoe::stream_fits(w1, H, 2 * I, block_size, true) &&
                              qmoe::stream_fits(w2, I, H, block_size, false);
     const bool expert_mode = !generic && !stream_mode && L.decode && E <= 64 && E <= R && H <= 2048 &&

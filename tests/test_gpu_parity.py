@@ -333,7 +333,7 @@ def test_layer_decode_expert_stationary(T, k, E, skew):
     _layer_check(spec, 40 + T + E, logits=logits)
 
 
-# Streamed decode: R = T*top_k <= 64, E <= R or E <= 16, 2/4-bit widths, K <= 2048 with
+# Streamed decode: R = T*top_k <= 64, E <= R or E <= 32, 2/4-bit widths, K <= 2048 with
 # whole 8-block scale units per row; cases cover both widths per projection,
 # RAW (block multiple of 128) and per-element dequant, one piece with a
 # clamped tail (K = 256 at 2 bits), eight pieces (4 bits, K = 2048), A rows
@@ -399,7 +399,8 @@ def test_layer_stream_decode_one_expert_sixteen_rows():
     _layer_check(spec, 1350, logits=logits)
 
 
-@pytest.mark.parametrize("T,E,k", [(8, 8, 2), (1, 8, 2), (3, 8, 2), (4, 16, 2), (16, 32, 4)])
+@pytest.mark.parametrize("T,E,k", [(8, 8, 2), (1, 8, 2), (3, 8, 2), (4, 16, 2), (16, 32, 4), (2, 32, 3),
+                                   (12, 32, 1)])
 def test_layer_stream_decode_expert_zero_unselected(T, E, k):
     # the first workgroup of the streamed fc1 writes every expert's offsets
     # and sorted routes; here its own expert (0) has no route.  A call with
