@@ -6,7 +6,7 @@ combinations the hand-written cases do not list; a second set adds random
 operator options (gate/up layouts with fc3, biases, router_weights, SwiGLU
 alpha/beta/limit).  Each layer is compared with the oracle on sampled
 tokens (first, last and random ones) at the layer bound of the other parity
-tests.  A third set draws small decode layers (at most 16 tokens and 16
+tests.  A third set draws small decode layers (at most 16 tokens and 32
 experts, 2/4-bit, K a power of two up to 2048), often with fewer routes than
 experts, for the streamed decode kernels; every fourth one keeps expert 0
 out of every token's choice.  Sizes are capped so that one case costs well
@@ -137,7 +137,7 @@ def _draw_stream(i: int) -> tuple[dict, np.ndarray | None]:
     bs = int(rng.choice([32, 64, 128, 256]))
     H = max(bs, int(rng.choice([128, 256, 512, 1024, 2048])))
     I = max(bs, int(rng.choice([128, 256, 512, 1024, 2048])))
-    E = int(rng.integers(2, 17))
+    E = int(rng.integers(2, 33))
     T = int(rng.choice([1, 1, 2, 2, 3, 4, 5, 8, 12, 16]))
     k = int(rng.integers(1, min(E, 4) + 1))
     b1, b2 = (int(b) for b in rng.choice([2, 4], size=2))
